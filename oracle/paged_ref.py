@@ -1,0 +1,237 @@
+"""Paged-KV cache write, attention and log-sum-exp merge, in fp64 (test infrastructure).
+
+Plain definitions, written for checking by eye against the pages:
+
+* cache write: vLLM PR #64064, sections "Tests" and "Details" -- each new token's
+  K goes to the first head_dim columns of its slot's row for every KV head, V to
+  its own head_dim_v columns at V's own offset, read with V's own head stride;
+  nothing else in the buffer (other slots, slack past the cache) changes.
+* paged addressing: key j of sequence b lives at block  block_tables[b, j // BS],
+  slot-in-block  j % BS  (the block-size / block-table convention the pages use).
+* attention: exact softmax attention per (query, q-head); GQA maps q-head h to
+  KV head h // (Hq // Hkv); a query at absolute position p sees keys 0..p.  Rows
+  with no visible key output 0 and lse = -inf (diffbot model card, section
+  "Update 2026-10-01": padded rows must come out 0, not NaN).
+* split-KV partials and their merge: the two-stage decode of vLLM PR #50371
+  (review thread: split sweep, runtime split count) and the split-KV reducer of
+  the diffbot model card; the merge is the log-sum-exp identity.
+
+fp8 caches are dequantised as code value x scale (per tensor or per KV head).
+Everything is float64; Q/K/V come in as the exact bf16 / fp8 values.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import e4m3fn
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    return e4m3fn.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float values to bf16 (nearest, ties to even) via exact integer arithmetic on binary32."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lower = u & 0xFFFF
+    upper = u >> 16
+    round_up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    out = (upper + round_up.astype(np.uint64)) & 0xFFFF
+    out = np.where(np.isnan(f), 0x7FC0, out)
+    return out.astype(np.uint16)
+
+
+class CacheSpec:
+    """Element offsets inside a flat cache buffer (strides in elements)."""
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, row_dim, head_dim_k, head_dim_v, v_offset,
+                 stride_block=None, stride_slot=None, stride_head=None, kv_dtype="bf16"):
+        self.num_blocks, self.block_size, self.num_kv_heads = num_blocks, block_size, num_kv_heads
+        self.row_dim, self.dk, self.dv, self.v_off = row_dim, head_dim_k, head_dim_v, v_offset
+        self.stride_head = row_dim if stride_head is None else stride_head
+        self.stride_slot = num_kv_heads * self.stride_head if stride_slot is None else stride_slot
+        self.stride_block = block_size * self.stride_slot if stride_block is None else stride_block
+        self.kv_dtype = kv_dtype
+
+    @classmethod
+    def from_geom(cls, g):
+        return cls(g.num_blocks, g.block_size, g.num_kv_heads, g.row_dim, g.head_dim_k, g.head_dim_v,
+                   g.v_offset, g.stride_block, g.stride_slot, g.stride_head, g.kv_dtype)
+
+    def row_offset(self, slot: int, head: int) -> int:
+        blk, pos = divmod(int(slot), self.block_size)
+        return blk * self.stride_block + pos * self.stride_slot + head * self.stride_head
+
+
+def _scale_for(scale, head):
+    if scale is None:
+        return np.float32(1.0)
+    s = np.asarray(scale, dtype=np.float32).reshape(-1)
+    return s[0] if s.size == 1 else s[head]
+
+
+def cache_write(cache_flat: np.ndarray, spec: CacheSpec, key_bits: np.ndarray,
+                value_bits: Optional[np.ndarray], slot_mapping: np.ndarray,
+                k_scale=None, v_scale=None) -> np.ndarray:
+    """Return a copy of ``cache_flat`` after writing every token with slot >= 0.
+
+    bf16 caches get the bf16 bit patterns unchanged; fp8 caches get
+    E4M3FN(fp32(x) / fp32(scale)) with K and V scales separate, each per tensor
+    ([1]) or per KV head ([Hkv]).
+    """
+    out = np.array(cache_flat, copy=True)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    live = np.nonzero(slots >= 0)[0]                           # slot -1: padding token, skipped
+    blk, pos = slots[live] // spec.block_size, slots[live] % spec.block_size
+    for h in range(spec.num_kv_heads):
+        base = blk * spec.stride_block + pos * spec.stride_slot + h * spec.stride_head   # [n]
+        k = np.asarray(key_bits)[live, h, : spec.dk]
+        if spec.kv_dtype == "fp8":
+            k = e4m3fn.quantize(k, _scale_for(k_scale, h))
+        out[base[:, None] + np.arange(spec.dk)[None, :]] = k
+        if value_bits is not None:
+            v = np.asarray(value_bits)[live, h, : spec.dv]
+            if spec.kv_dtype == "fp8":
+                v = e4m3fn.quantize(v, _scale_for(v_scale, h))
+            out[base[:, None] + spec.v_off + np.arange(spec.dv)[None, :]] = v
+    return out
+
+
+def decode_cache(cache_flat: np.ndarray, spec: CacheSpec) -> np.ndarray:
+    """Element values of the whole cache buffer as float64 (no scale applied)."""
+    if spec.kv_dtype == "fp8":
+        return e4m3fn.decode(np.asarray(cache_flat, dtype=np.uint8))
+    return bf16_to_f64(np.asarray(cache_flat).view(np.uint16))
+
+
+def gather_kv(values_flat: np.ndarray, spec: CacheSpec, block_table_row: np.ndarray, seq_len: int,
+              k_scale=None, v_scale=None):
+    """Dense K [S, Hkv, Dk] and V [S, Hkv, Dv] of one sequence through its block table."""
+    S, H = int(seq_len), spec.num_kv_heads
+    K = np.empty((S, H, spec.dk), dtype=np.float64)
+    V = np.empty((S, H, spec.dv), dtype=np.float64)
+    if S == 0:
+        return K, V
+    j = np.arange(S)
+    blocks = np.asarray(block_table_row, dtype=np.int64)[j // spec.block_size]
+    slot_base = blocks * spec.stride_block + (j % spec.block_size) * spec.stride_slot
+    for h in range(H):
+        base = slot_base + h * spec.stride_head
+        K[:, h, :] = values_flat[base[:, None] + np.arange(spec.dk)[None, :]] * float(_scale_for(k_scale, h))
+        V[:, h, :] = values_flat[base[:, None] + spec.v_off + np.arange(spec.dv)[None, :]] \
+            * float(_scale_for(v_scale, h))
+    return K, V
+
+
+def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray, scale: float,
+                   key_range=None):
+    """Softmax attention of query rows of ONE sequence.
+
+    q [L, Hq, Dk] float64, K [S, Hkv, Dk], V [S, Hkv, Dv]; query l sits at absolute
+    position positions[l] and sees keys j <= positions[l] (restricted to
+    ``key_range`` = [lo, hi) when given, for split-KV partials).
+    Returns out [L, Hq, Dv] (0 for rows without visible keys) and lse [L, Hq]
+    (natural log, -inf for those rows).
+    """
+    L, Hq, _ = q.shape
+    S, Hkv, Dv = V.shape
+    G = Hq // Hkv
+    lo, hi = (0, S) if key_range is None else key_range
+    out = np.zeros((L, Hq, Dv), dtype=np.float64)
+    lse = np.full((L, Hq), -np.inf, dtype=np.float64)
+    keys = np.arange(lo, hi)
+    for h in range(Hq):
+        g = h // G                                             # GQA: consecutive q-heads share a KV head
+        s = scale * (q[:, h, :] @ K[lo:hi, g, :].T)            # [L, hi-lo]
+        visible = keys[None, :] <= np.asarray(positions)[:, None]
+        s = np.where(visible, s, -np.inf)
+        m = s.max(axis=1, initial=-np.inf)
+        has = np.isfinite(m)
+        w = np.where(visible & has[:, None], np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
+        l = w.sum(axis=1)
+        out[has, h, :] = (w[has] @ V[lo:hi, g, :]) / l[has, None]
+        lse[has, h] = m[has] + np.log(l[has])
+    return out, lse
+
+
+def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables, cache_flat: np.ndarray,
+                    spec: CacheSpec, scale: float, k_scale=None, v_scale=None, rows: Optional[Sequence[int]] = None):
+    """Attention of every query token (or of the token ids in ``rows``) over the paged cache.
+
+    Query i of sequence b (i < L_b = qsl[b+1] - qsl[b]) sits at position S_b - L_b + i:
+    seq_lens count the step's new tokens, which are in the cache before attention.
+    Returns (out [T or len(rows), Hq, Dv], lse [.., Hq]).
+    """
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    vals = decode_cache(cache_flat, spec)
+    q = bf16_to_f64(np.asarray(q_bits).view(np.uint16))
+    T, Hq = q.shape[0], q.shape[1]
+    want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(want), Hq, spec.dv), dtype=np.float64)
+    lse = np.full((len(want), Hq), -np.inf, dtype=np.float64)
+    for b in range(len(seq_lens)):
+        t0, t1 = int(qsl[b]), int(qsl[b + 1])
+        sel = np.nonzero((want >= t0) & (want < t1))[0]
+        if sel.size == 0:
+            continue
+        S, L = int(seq_lens[b]), t1 - t0
+        K, V = gather_kv(vals, spec, block_tables[b], S, k_scale, v_scale)
+        pos = S - L + (want[sel] - t0)
+        o, l = attention_rows(q[want[sel]], K, V, pos, scale)
+        out[sel], lse[sel] = o, l
+    return out, lse
+
+
+def partition_ranges(seq_len: int, num_partitions: int, block_size: int):
+    """Key ranges of split-KV partitions: chunk = ceil(S / P) rounded up to a multiple of BS."""
+    if seq_len == 0:
+        return [(0, 0)] * num_partitions
+    chunk = math.ceil(math.ceil(seq_len / num_partitions) / block_size) * block_size
+    return [(min(p * chunk, seq_len), min((p + 1) * chunk, seq_len)) for p in range(num_partitions)]
+
+
+def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, cache_flat, spec, scale,
+                             num_partitions, k_scale=None, v_scale=None):
+    """Per-partition normalised outputs [T, Hq, P, Dv] and lse [T, Hq, P] (empty -> 0, -inf)."""
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    vals = decode_cache(cache_flat, spec)
+    q = bf16_to_f64(np.asarray(q_bits).view(np.uint16))
+    T, Hq = q.shape[0], q.shape[1]
+    P = num_partitions
+    po = np.zeros((T, Hq, P, spec.dv), dtype=np.float64)
+    pl = np.full((T, Hq, P), -np.inf, dtype=np.float64)
+    for b in range(len(seq_lens)):
+        t0, t1 = int(qsl[b]), int(qsl[b + 1])
+        S, L = int(seq_lens[b]), t1 - t0
+        K, V = gather_kv(vals, spec, block_tables[b], S, k_scale, v_scale)
+        pos = S - L + np.arange(L)
+        for p, rng in enumerate(partition_ranges(S, P, spec.block_size)):
+            if rng[1] <= rng[0]:
+                continue
+            o, l = attention_rows(q[t0:t1], K, V, pos, scale, key_range=rng)
+            po[t0:t1, :, p, :], pl[t0:t1, :, p] = o, l
+    return po, pl
+
+
+def merge_lse(part_out: np.ndarray, part_lse: np.ndarray):
+    """Combine split-KV partials: out = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p - max lse).
+
+    A row whose partials are all empty (max lse = -inf) gives out = 0, lse = -inf, never NaN.
+    """
+    po = np.asarray(part_out, dtype=np.float64)
+    pl = np.asarray(part_lse, dtype=np.float64)
+    M = pl.max(axis=-1)
+    has = np.isfinite(M)
+    Msafe = np.where(has, M, 0.0)
+    w = np.where(np.isfinite(pl), np.exp(pl - Msafe[..., None]), 0.0)
+    den = w.sum(axis=-1)
+    out = np.zeros(po.shape[:-2] + po.shape[-1:], dtype=np.float64)
+    num = (w[..., None] * po).sum(axis=-2)
+    out[has] = num[has] / den[has][..., None]
+    lse = np.where(has, Msafe + np.log(np.where(has, den, 1.0)), -np.inf)
+    return out, lse
