@@ -1,0 +1,219 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged-KV attention library.
+ *
+ * Paged-KV attention with asymmetric K/V head dims, and the cache write that
+ * feeds it.  Two row layouts are served by one descriptor:
+ *   - the packed DiffKV row: per KV head one row of head_dim_k + head_dim_v
+ *     elements, K in the first head_dim_k columns and V in the next head_dim_v
+ *     (MiMo-V2.6: 192 + 128, 4 KV heads; vLLM PR #64064 "[...] asymmetric K/V",
+ *     sections "Overview", "Tests", "Details");
+ *   - the shared MLA latent row: one KV head of 576 elements whose first 512
+ *     columns are also V (12 query heads per rank; vLLM PR #50371 "[ROCm] Enable
+ *     12-head MLA persistent decode", sections "Purpose", "Test Plan").
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after a call returns and never allocates, frees, reads
+ *     device memory on the host, or synchronises: every call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream).  The caller
+ *     keeps the buffers alive until that work completes.
+ *   - Strides are in ELEMENTS of the tensor they describe.
+ *   - Status: ATTN_OK, or ATTN_E_INVALID for bad host-side arguments (null
+ *     pointers, negative sizes, inconsistent geometry, a workspace that is too
+ *     small), ATTN_E_UNSUPPORTED when no kernel exists for a shape or dtype
+ *     (the caller falls back, as a backend that cannot serve a head-size pair
+ *     does in vLLM PR #64064, "Known limitations"), ATTN_E_HIP when the HIP
+ *     runtime reports a launch error.  Nothing aborts or throws across the ABI;
+ *     attn_last_error() gives a thread-local message for the last non-OK status.
+ *   - Device-resident values are PRECONDITIONS, not checked by the library:
+ *     every slot < num_blocks * block_size, every block id < num_blocks, no two
+ *     tokens write the same slot, seq_len <= bt_stride * block_size, and the
+ *     block-table entries a sequence uses are valid.  Entries past
+ *     ceil(seq_len / block_size) are never read.
+ *   - Numerics: Q, K, V are bf16 (or fp8 E4M3FN cache bytes); dot products and
+ *     softmax in fp32; output bf16 (round to nearest even); LSE natural log, fp32.
+ *     Query head h uses KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,
+  ATTN_E_UNSUPPORTED = 2,
+  ATTN_E_HIP = 3
+} attn_status;
+
+/* Cache element type.  FP8 is the OCP E4M3FN byte format (no infinities, 0x7F /
+ * 0xFF NaN, max finite 448); the diffbot MiMo-V2.6-Flash model card ("FP8 (E4M3)
+ * KV cache") and vLLM PR #64064 ("Tests": bf16 and fp8 caches). */
+typedef enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3FN = 1 } attn_kv_dtype;
+
+/* fp8 dequantisation scales: one fp32 per tensor ([1]) or one per KV head
+ * ([num_kv_heads]), separate for K and V (vLLM PR #64064, "Tests": per-tensor
+ * and per-head scales).  Ignored for bf16 caches. */
+typedef enum { ATTN_SCALE_NONE = 0, ATTN_SCALE_PER_TENSOR = 1, ATTN_SCALE_PER_HEAD = 2 } attn_scale_mode;
+
+/* Paged KV cache descriptor.
+ * Element (block b, slot-in-block s, KV head h, column c) lives at
+ *   data + b*stride_block + s*stride_slot + h*stride_head + c        (elements)
+ * Key j of a sequence with block table row bt is in block bt[j / block_size],
+ * slot j % block_size.  K occupies columns [0, head_dim_k), V occupies
+ * [v_offset, v_offset + head_dim_v); both must fit in row_dim.  The default
+ * (NHD) strides are stride_head = row_dim, stride_slot = num_kv_heads*row_dim,
+ * stride_block = block_size*stride_slot.
+ * DiffKV: row_dim 320, head_dim_k 192, head_dim_v 128, v_offset 192.
+ * MLA:    row_dim 576, head_dim_k 576, head_dim_v 512, v_offset 0.          */
+typedef struct {
+  void* data;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t row_dim;
+  int32_t head_dim_k;
+  int32_t head_dim_v;
+  int32_t v_offset;
+  int32_t reserved0;
+  int64_t stride_block;
+  int64_t stride_slot;
+  int64_t stride_head;
+  attn_kv_dtype dtype;
+  attn_scale_mode scale_mode;
+  const float* k_scale; /* device, [1] or [num_kv_heads]; NULL iff scale_mode NONE */
+  const float* v_scale; /* device, [1] or [num_kv_heads]; NULL iff scale_mode NONE */
+} attn_cache_desc;
+
+/* ---------------------------------------------------------------------------
+ * attn_cache_write -- write new tokens' K and V into their cache slots.
+ * vLLM PR #64064, sections "Claims" and "Details": V is read with ITS OWN head
+ * stride and written with ITS OWN width head_dim_v at column v_offset, not with
+ * K's; section "Tests": the cache must match one built slot by slot, K in the
+ * first head_dim_k columns of a row and V in the remaining head_dim_v, and the
+ * bytes past the cache end stay untouched.
+ *
+ *   key    [num_tokens, num_kv_heads, head_dim_k] bf16; element (t,h,d) at
+ *          key + t*key_stride_tok + h*key_stride_head + d.
+ *   value  [num_tokens, num_kv_heads, head_dim_v] bf16, own strides; may be
+ *          NULL, then only the K columns are written (MLA latent rows, whose V
+ *          is the row's first head_dim_v columns).
+ *   slot_mapping [num_tokens] int64: slot = block*block_size + slot-in-block;
+ *          -1 skips the token (padding).
+ *   For ATTN_KV_FP8_E4M3FN the stored byte is E4M3FN(fp32(x) / fp32(scale)):
+ *   correctly rounded binary32 division, round to nearest even, saturation to
+ *   +-448, NaN -> 0x7F, signed zero kept.  bf16 caches get the bits unchanged.
+ *   num_tokens == 0 is a no-op.                                              */
+attn_status attn_cache_write(const void* key, int64_t key_stride_tok, int64_t key_stride_head,
+                             const void* value, int64_t val_stride_tok, int64_t val_stride_head,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             const attn_cache_desc* cache, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Split-KV workspace.  Partials of `rows` query rows over num_partitions key
+ * ranges: part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 (each
+ * normalised by its own softmax sum) followed by part_lse [rows, num_q_heads,
+ * num_partitions] fp32 (-inf for an empty range), starting at the workspace's
+ * first byte, then a small area of per-(row-group) counters.  Returns the bytes
+ * needed (0 for invalid arguments).                                            */
+size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim_v,
+                                    int32_t num_partitions);
+
+/* ---------------------------------------------------------------------------
+ * attn_decode_splitkv -- one query token per sequence over its paged context.
+ * Split-KV (flash-decoding) with a runtime, device-side choice of each
+ * partition's key range and a log-sum-exp merge: vLLM PR #50371, review thread
+ * (two-stage decode, split count derived from device-side sequence lengths with
+ * a graph-stable launch shape; 100K context best near 96 splits); diffbot model
+ * card, "What the kernels do" (split-KV needed to fill the GPU at long context).
+ * GQA: the num_q_heads/num_kv_heads query heads of a KV head share each K/V read.
+ *
+ *   q        [num_seqs, num_q_heads, head_dim_k] bf16, element (b,h,d) at
+ *            q + b*q_stride_tok + h*q_stride_head + d.  The query of sequence b
+ *            is at position seq_lens[b]-1 and sees keys 0..seq_lens[b]-1.
+ *   block_tables [num_seqs, bt_stride] int32; seq_lens [num_seqs] int32 >= 0.
+ *   softmax_scale  multiplies q.k (fp32), e.g. 1/sqrt(head_dim_k).
+ *   num_partitions P >= 1: each sequence's keys are cut into P ranges of
+ *            ceil(seq_len/P) keys (rounded up to the kernel's 16-key tile).
+ *   workspace      >= attn_splitkv_workspace_bytes(num_seqs, num_q_heads,
+ *            head_dim_v, P) bytes of device memory, 256-byte aligned.
+ *   out      [num_seqs, num_q_heads, head_dim_v] bf16 contiguous.  If out is
+ *            NULL only the partials are produced, left in the workspace for
+ *            attn_merge_lse (e.g. after partials of other key ranges are added).
+ *   out_lse  [num_seqs, num_q_heads] fp32 or NULL.
+ *   A sequence with seq_len 0 outputs exact zeros and lse -inf.             */
+attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                int32_t num_seqs, int32_t num_q_heads,
+                                const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
+                                void* workspace, size_t workspace_bytes,
+                                void* out, float* out_lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_merge_lse -- combine split-KV partials.  Per (row, head): M = max_p lse_p;
+ * if M = -inf (no partition saw a key) out = 0 and lse = -inf, never NaN (the
+ * empty-row fix of the split-KV reducer: diffbot model card, "Update
+ * 2026-10-01"); otherwise w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p,
+ * lse = M + ln sum w_p.
+ *   part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 contiguous;
+ *   part_lse [rows, num_q_heads, num_partitions] fp32 contiguous;
+ *   out [rows, num_q_heads, head_dim_v] bf16 contiguous; out_lse fp32 or NULL. */
+attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t rows, int32_t num_q_heads,
+                           int32_t head_dim_v, int32_t num_partitions,
+                           void* out, float* out_lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_prefill_causal -- causal attention of a batch of query chunks over the
+ * paged cache (chunked prefill: 4096-token chunks, FA2-style tiles, GQA heads
+ * sharing each K/V tile; diffbot model card, "What the kernels do").  The
+ * chunk's K/V must already be in the cache (attn_cache_write first).
+ *   q [num_tokens, num_q_heads, head_dim_k] bf16 with token/head strides.
+ *   query_start_loc [num_seqs+1] int32: tokens of sequence b are
+ *            query_start_loc[b] .. query_start_loc[b+1]-1; L_b is their count.
+ *   seq_lens [num_seqs] int32: keys of sequence b INCLUDING this chunk; query i
+ *            of b sits at position seq_lens[b] - L_b + i and sees keys 0..that.
+ *   max_query_len  >= every L_b (sizes the launch).
+ *   out [num_tokens, num_q_heads, head_dim_v] bf16 contiguous; out_lse
+ *            [num_tokens, num_q_heads] fp32 or NULL.
+ *   Rows with no visible key output 0 and lse -inf.                            */
+attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                int32_t max_query_len, int32_t num_q_heads,
+                                const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* seq_lens, float softmax_scale,
+                                void* out, float* out_lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_verify -- speculative-decode verify: a few query tokens per sequence
+ * (e.g. 3 drafts + 1), causal among themselves, over a long paged context, with
+ * split-KV kept for query_len > 1 and all query rows of a KV head sharing one
+ * K/V read (diffbot model card, "What the kernels do" and "Benchmarks": "one
+ * program per whole verify"); fp8 K/V converted to bf16 in the load path, the
+ * scales applied after the dot products (Q stays bf16: fp8 QK^T was rejected,
+ * "Benchmarks").  Padded rows (seq_len 0) output exact zeros ("Update
+ * 2026-10-01").  Arguments as attn_prefill_causal, plus the split-KV
+ * num_partitions and workspace as attn_decode_splitkv (rows = num_tokens).
+ * max_query_len * (num_q_heads/num_kv_heads) must be <= 64.                    */
+attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                        const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                        int32_t max_query_len, int32_t num_q_heads,
+                        const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
+                        void* workspace, size_t workspace_bytes,
+                        void* out, float* out_lse, void* stream);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_H */

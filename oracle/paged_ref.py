@@ -102,15 +102,19 @@ def cache_write(cache_flat: np.ndarray, spec: CacheSpec, key_bits: np.ndarray,
 
 
 def decode_cache(cache_flat: np.ndarray, spec: CacheSpec) -> np.ndarray:
-    """Element values of the whole cache buffer as float64 (no scale applied)."""
+    """Values of raw cache elements as float64 (no scale applied)."""
     if spec.kv_dtype == "fp8":
         return e4m3fn.decode(np.asarray(cache_flat, dtype=np.uint8))
     return bf16_to_f64(np.asarray(cache_flat).view(np.uint16))
 
 
-def gather_kv(values_flat: np.ndarray, spec: CacheSpec, block_table_row: np.ndarray, seq_len: int,
+def gather_kv(cache_flat: np.ndarray, spec: CacheSpec, block_table_row: np.ndarray, seq_len: int,
               k_scale=None, v_scale=None):
-    """Dense K [S, Hkv, Dk] and V [S, Hkv, Dv] of one sequence through its block table."""
+    """Dense K [S, Hkv, Dk] and V [S, Hkv, Dv] of one sequence through its block table.
+
+    ``cache_flat`` holds the raw cache elements (bf16 bit patterns or E4M3FN bytes);
+    only the gathered elements are decoded, then multiplied by the K / V scale.
+    """
     S, H = int(seq_len), spec.num_kv_heads
     K = np.empty((S, H, spec.dk), dtype=np.float64)
     V = np.empty((S, H, spec.dv), dtype=np.float64)
@@ -121,9 +125,10 @@ def gather_kv(values_flat: np.ndarray, spec: CacheSpec, block_table_row: np.ndar
     slot_base = blocks * spec.stride_block + (j % spec.block_size) * spec.stride_slot
     for h in range(H):
         base = slot_base + h * spec.stride_head
-        K[:, h, :] = values_flat[base[:, None] + np.arange(spec.dk)[None, :]] * float(_scale_for(k_scale, h))
-        V[:, h, :] = values_flat[base[:, None] + spec.v_off + np.arange(spec.dv)[None, :]] \
-            * float(_scale_for(v_scale, h))
+        k_raw = cache_flat[base[:, None] + np.arange(spec.dk)[None, :]]
+        v_raw = cache_flat[base[:, None] + spec.v_off + np.arange(spec.dv)[None, :]]
+        K[:, h, :] = decode_cache(k_raw, spec) * float(_scale_for(k_scale, h))
+        V[:, h, :] = decode_cache(v_raw, spec) * float(_scale_for(v_scale, h))
     return K, V
 
 
@@ -168,7 +173,6 @@ def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables,
     """
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
-    vals = decode_cache(cache_flat, spec)
     q = bf16_to_f64(np.asarray(q_bits).view(np.uint16))
     T, Hq = q.shape[0], q.shape[1]
     want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -180,7 +184,7 @@ def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables,
         if sel.size == 0:
             continue
         S, L = int(seq_lens[b]), t1 - t0
-        K, V = gather_kv(vals, spec, block_tables[b], S, k_scale, v_scale)
+        K, V = gather_kv(cache_flat, spec, block_tables[b], S, k_scale, v_scale)
         pos = S - L + (want[sel] - t0)
         o, l = attention_rows(q[want[sel]], K, V, pos, scale)
         out[sel], lse[sel] = o, l
@@ -199,7 +203,6 @@ def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, ca
                              num_partitions, k_scale=None, v_scale=None):
     """Per-partition normalised outputs [T, Hq, P, Dv] and lse [T, Hq, P] (empty -> 0, -inf)."""
     qsl = np.asarray(query_start_loc, dtype=np.int64)
-    vals = decode_cache(cache_flat, spec)
     q = bf16_to_f64(np.asarray(q_bits).view(np.uint16))
     T, Hq = q.shape[0], q.shape[1]
     P = num_partitions
@@ -208,7 +211,7 @@ def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, ca
     for b in range(len(seq_lens)):
         t0, t1 = int(qsl[b]), int(qsl[b + 1])
         S, L = int(seq_lens[b]), t1 - t0
-        K, V = gather_kv(vals, spec, block_tables[b], S, k_scale, v_scale)
+        K, V = gather_kv(cache_flat, spec, block_tables[b], S, k_scale, v_scale)
         pos = S - L + np.arange(L)
         for p, rng in enumerate(partition_ranges(S, P, spec.block_size)):
             if rng[1] <= rng[0]:

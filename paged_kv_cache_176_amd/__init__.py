@@ -1,0 +1,19 @@
+"""Paged-KV attention for AMD MI355X (gfx950): thin Python binding of ``libpagedattn.so``.
+
+The binding only marshals arguments (tensor data pointers, strides, the current
+HIP stream) into the C ABI declared in ``include/pagedattn.h``; every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device memory
+and streams.  If the library is missing the calls raise: there is no fallback.
+"""
+from .ops import (  # noqa: F401
+    AttnError,
+    CacheDesc,
+    cache_write,
+    decode_splitkv,
+    load_library,
+    merge_lse,
+    prefill_causal,
+    splitkv_workspace_bytes,
+    verify,
+    library_path,
+)

@@ -1,0 +1,118 @@
+// Cache write: new tokens' K and V into their paged slots.
+//
+// V is addressed with its own head stride and written with its own width at its
+// own column offset (vLLM PR #64064, "Details": the symmetric kernel reused K's
+// head stride and element count for V).  bf16 caches receive the bits unchanged;
+// fp8 caches receive E4M3FN(fp32(x) / fp32(scale)), round to nearest even,
+// saturating at +-448 (reading of the pages' "fp8 E4M3 cache, per-tensor and
+// per-head scales").
+//
+// One thread moves one 8-element vector (16 B of bf16 in; 16 B bf16 or 8 B fp8
+// out).  The thread -> (token, head, vector) mapping is token-major so that a
+// wave covers whole rows and its loads and stores are contiguous.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+// binary32 -> E4M3FN byte: nearest, ties to even, saturating, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3fn_from_f32(float q) {
+  uint32_t u = __float_as_uint(q);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;                 // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |q| >= 448 or inf: saturate
+  if (a >= 0x3C800000u) {                            // |q| >= 2^-6: normal E4M3FN
+    // keep 3 of the 23 mantissa bits, ties to even on the 20 dropped bits;
+    // a carry out of the mantissa bumps the exponent, as it should
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));         // rebias 127 -> 7
+  }
+  // subnormal range: multiples of 2^-9; |q| * 512 is exact, rint is ties-to-even
+  float m = __builtin_rintf(__builtin_fabsf(q) * 512.0f);
+  return sign | (uint32_t)m;                          // m = 8 is 0x08 = 2^-6, correct
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <bool FP8, bool VEC>
+__global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
+  const int nk = VEC ? a.c.dk / 8 : a.c.dk;          // vectors (or elements) per head for K
+  const int nv = a.value ? (VEC ? a.c.dv / 8 : a.c.dv) : 0;
+  const int per_head = nk + nv;
+  const int per_tok = per_head * a.c.num_kv_heads;
+  const int64_t total = (int64_t)per_tok * a.num_tokens;
+  for (int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; item < total;
+       item += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(item / per_tok);
+    const int r = (int)(item - (int64_t)t * per_tok);
+    const int h = r / per_head;
+    const int c = r - h * per_head;
+    const int64_t slot = a.slots[t];
+    if (slot < 0) continue;                          // padding token
+    const int64_t blk = slot / a.c.block_size;
+    const int64_t pos = slot - blk * a.c.block_size;
+    const int64_t row = blk * a.c.sb + pos * a.c.ss + (int64_t)h * a.c.sh;   // elements
+    const bool isk = c < nk;
+    const int e0 = VEC ? (isk ? c : c - nk) * 8 : (isk ? c : c - nk);      // element in K or V
+    const uint16_t* src = isk ? a.key + (int64_t)t * a.k_st + (int64_t)h * a.k_sh + e0
+                              : a.value + (int64_t)t * a.v_st + (int64_t)h * a.v_sh + e0;
+    const int64_t dst_el = row + (isk ? 0 : a.c.v_off) + e0;
+    if constexpr (!FP8) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.c.data) + dst_el;
+      if constexpr (VEC) *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      else *dst = *src;
+    } else {
+      const float* sp = isk ? a.c.k_scale : a.c.v_scale;
+      const float scale = a.c.scale_mode == 2 ? sp[h] : sp[0];
+      uint8_t* dst = a.c.data + dst_el;
+      if constexpr (VEC) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t w = x[i];
+          uint32_t b0 = e4m3fn_from_f32(bf16_bits_to_f32(w & 0xFFFFu) / scale);
+          uint32_t b1 = e4m3fn_from_f32(bf16_bits_to_f32(w >> 16) / scale);
+          uint32_t pair = b0 | (b1 << 8);
+          if (i < 2) lo |= pair << (16 * i);
+          else hi |= pair << (16 * (i - 2));
+        }
+        u32x2 o;
+        o[0] = lo;
+        o[1] = hi;
+        *reinterpret_cast<u32x2*>(dst) = o;
+      } else {
+        *dst = (uint8_t)e4m3fn_from_f32(bf16_bits_to_f32(*src) / scale);
+      }
+    }
+  }
+}
+
+bool launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
+  const bool fp8 = a.c.esize == 1;
+  // 8-element vectors need 16-byte aligned sources and 16 B (bf16) / 8 B (fp8)
+  // aligned destinations for every (token, head, vector).
+  auto al = [](const void* p, int n) { return ((uintptr_t)p % n) == 0; };
+  const int dst_align = fp8 ? 8 : 16;
+  bool vec = a.c.dk % 8 == 0 && al(a.key, 16) && a.k_st % 8 == 0 && a.k_sh % 8 == 0 &&
+             al(a.c.data, dst_align) && a.c.sb % 8 == 0 && a.c.ss % 8 == 0 && a.c.sh % 8 == 0;
+  if (a.value) vec = vec && a.c.dv % 8 == 0 && a.c.v_off % 8 == 0 && al(a.value, 16) && a.v_st % 8 == 0 &&
+                     a.v_sh % 8 == 0;
+  const int per = vec ? (a.c.dk + (a.value ? a.c.dv : 0)) / 8 : (a.c.dk + (a.value ? a.c.dv : 0));
+  const int64_t total = (int64_t)per * a.c.num_kv_heads * a.num_tokens;
+  if (total == 0) return true;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  dim3 grid((unsigned)blocks), block(256);
+  if (fp8) {
+    if (vec) hipLaunchKernelGGL((cache_write_kernel<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((cache_write_kernel<true, false>), grid, block, 0, s, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((cache_write_kernel<false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((cache_write_kernel<false, false>), grid, block, 0, s, a);
+  }
+  return true;
+}
+
+}  // namespace pa

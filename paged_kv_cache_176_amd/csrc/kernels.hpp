@@ -1,0 +1,66 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Host-side argument checking is done before these are called; the launchers
+// only pick a template instance and enqueue on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct CacheView {
+  uint8_t* data;        // base of the cache (bytes)
+  int32_t num_blocks, block_size, num_kv_heads, row_dim;
+  int32_t dk, dv, v_off;
+  int64_t sb, ss, sh;   // strides in elements
+  int32_t esize;        // 2 (bf16) or 1 (fp8)
+  int32_t scale_mode;   // 0 none, 1 per tensor, 2 per head
+  const float* k_scale;
+  const float* v_scale;
+};
+
+struct CacheWriteArgs {
+  const uint16_t* key; int64_t k_st, k_sh;
+  const uint16_t* value; int64_t v_st, v_sh;   // value may be null
+  const int64_t* slots; int32_t num_tokens;
+  CacheView c;
+};
+
+// Returns false if no kernel instance matches (caller reports UNSUPPORTED).
+bool launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+
+struct SplitArgs {
+  const uint16_t* q; int64_t q_st, q_sh;
+  const int32_t* qsl;       // null: row b is sequence b with one query
+  int32_t num_seqs, num_q_heads, max_q;
+  CacheView c;
+  const int32_t* bt; int32_t bt_stride;
+  const int32_t* seq_lens;
+  float scale;
+  int32_t num_partitions;
+  float* part_out; float* part_lse;
+  int32_t rows;             // total query rows (tokens)
+};
+
+bool splitkv_supported(const SplitArgs& a);
+bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s);
+
+struct MergeArgs {
+  const float* part_out; const float* part_lse;
+  int32_t rows, num_q_heads, dv, num_partitions;
+  uint16_t* out; float* out_lse;
+};
+bool launch_merge(const MergeArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+  const uint16_t* q; int64_t q_st, q_sh;
+  const int32_t* qsl; int32_t num_seqs, num_tokens, max_q, num_q_heads;
+  CacheView c;
+  const int32_t* bt; int32_t bt_stride;
+  const int32_t* seq_lens;
+  float scale;
+  uint16_t* out; float* out_lse;
+};
+bool prefill_supported(const PrefillArgs& a);
+bool launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,394 @@
+// Split-KV paged attention: per (partition, KV head, sequence) one workgroup
+// computes the softmax-normalised partial output and log-sum-exp of every query
+// row that uses this KV head, over the partition's key range.
+//
+// Serves three shapes with one body (the "rows" of a KV head are its query
+// tokens x its GQA query heads, row r = token_index * G + head_in_group):
+//   decode  1 token x G heads        (G = 8 for MiMo's 32/4 heads)
+//   verify  L tokens x G heads       (L = 4: 3 drafts + 1, causal among themselves)
+//   MLA     1 token x 12 heads over one 576-wide latent row, V = its first 512
+// Prior art on the pages: split-KV two-stage decode with a device-side,
+// graph-stable split count (vLLM PR #50371, review thread), split-KV kept for
+// multi-token verify and one program per whole verify so every row of a KV head
+// shares one K/V read (diffbot MiMo-V2.6-Flash model card, "Benchmarks" and
+// "What the kernels do").
+//
+// gfx950 mapping (wave64, MFMA):
+//   QK^T   S^T[16 keys x 16 rows] += K[16 keys x 32 dims] * Q^T[32 dims x 16 rows]
+//          v_mfma_f32_16x16x32_bf16.  The K operand (lane: key l%16, dims
+//          8*(l/16)..+8) is exactly one 16-byte load of the cache row, so K goes
+//          HBM -> VGPR -> MFMA with no LDS.  Q lives in VGPRs for the whole run.
+//   softmax each lane holds 4 keys of one row; the row max / sum need two
+//          cross-group shuffles.  exp2 with log2(e) folded into the scale.
+//   PV     O^T[16 dims x 16 rows] += V^T[16 dims x 16 keys] * P^T[16 keys x 16 rows]
+//          v_mfma_f32_16x16x16_bf16.  P^T is the lane's own 4 probabilities
+//          (same lane layout as the S^T output); V^T comes from a per-wave LDS
+//          tile through ds_read_b64_tr_b16 (a transposing LDS read).
+//   fp8 K/V are converted to bf16 in the load path (exact); the K scale is
+//   applied to the fp32 scores, the V scale to the final output.
+// Work split: the workgroup's NW waves take interleaved 16-key tiles of the
+// partition with double-buffered register prefetch, then merge their (m, l,
+// acc) through LDS in a fixed order (deterministic).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+template <int DK, int DV, int VOFF, bool FP8>
+struct TileRegs {
+  static constexpr bool kVInK = !FP8 && (VOFF + DV <= DK) && (VOFF % 32 == 0);
+  static constexpr int kK = FP8 ? DK / 64 : DK / 32;          // 16-byte K loads per lane
+  static constexpr int kV = kVInK ? 1 : (FP8 ? DV / 64 : DV / 32);   // 16-byte V loads per lane
+  u32x4 k[kK];
+  u32x4 v[kV];
+};
+
+template <int DK, int DV, int VOFF, int NR, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
+  using Regs = TileRegs<DK, DV, VOFF, FP8>;
+  constexpr int KS = DK / 32;        // MFMA k-steps of QK^T
+  constexpr int DB = DV / 16;        // 16-dim blocks of PV
+  constexpr int VP = DV + 16;        // LDS row pitch of the V tile (elements), 32 B pad
+  constexpr int ROWS = NR * 16;
+  constexpr int VTILE = 16 * VP;     // elements per wave's V tile
+  constexpr int MERGE_PITCH = DV + 4;
+  constexpr int LDS_V = NW * VTILE * 2;
+  constexpr int LDS_M = NW * ROWS * 2 * 4 + ROWS * MERGE_PITCH * 4;
+  constexpr int LDS_BYTES = LDS_V > LDS_M ? LDS_V : LDS_M;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int P = a.num_partitions;
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const int S = a.seq_lens[b];
+  const int q0 = a.qsl ? a.qsl[b] : b;
+  const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
+  const int chunk = ceil_div(ceil_div(S, P), 16) * 16;
+  const int start = min(part * chunk, S);
+  const int end = min(start + chunk, S);
+  const int nt = ceil_div(end - start, 16);
+
+  // ---- Q rows of this KV head into registers (B operand of QK^T) ----
+  bf16x8 qreg[NR][KS];
+  int hi[NR];                                   // last visible key of the lane's row
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    const int r = rg * 16 + n;
+    const int qi = r / G, hh = r - qi * G;
+    const bool live = qi < L && qi < a.max_q;
+    hi[rg] = live ? min(S - L + qi, end - 1) : -1;
+    const uint16_t* qp = a.q + (int64_t)(q0 + (live ? qi : 0)) * a.q_st + (int64_t)(kvh * G + hh) * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // k-step ks covers dims {base(ks, g') .. +8 : g' = 0..3}; fp8 pairs k-steps so
+      // that one 16-byte load of 16 fp8 values feeds two of them
+      const int d0 = FP8 ? (ks >> 1) * 64 + g * 16 + (ks & 1) * 8 : ks * 32 + g * 8;
+      u32x4 w = {0, 0, 0, 0};
+      if (live) w = *reinterpret_cast<const u32x4*>(qp + d0);
+      qreg[rg][ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if (FP8 && a.c.scale_mode != 0) {
+    kscale = a.c.scale_mode == 2 ? a.c.k_scale[kvh] : a.c.k_scale[0];
+    vscale = a.c.scale_mode == 2 ? a.c.v_scale[kvh] : a.c.v_scale[0];
+  }
+  const float sl2 = a.scale * kLog2e * kscale;
+
+  f32x4 acc[NR][DB];
+  float m[NR], l[NR];
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    m[rg] = kNegInf;
+    l[rg] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * VTILE;
+  const uint8_t* cbase = a.c.data;
+  const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+  const int esz = FP8 ? 1 : 2;
+
+  auto load_tile = [&](Regs& R, int ti) {
+    const int j = min(start + ti * 16 + n, S - 1);          // clamp: never past the sequence
+    const int64_t blk = btrow[j / a.c.block_size];
+    const int64_t pos = j % a.c.block_size;
+    const uint8_t* row = cbase + (blk * a.c.sb + pos * a.c.ss + (int64_t)kvh * a.c.sh) * esz;
+#pragma unroll
+    for (int i = 0; i < Regs::kK; ++i)
+      R.k[i] = *reinterpret_cast<const u32x4*>(row + (FP8 ? i * 64 + g * 16 : (i * 32 + g * 8) * 2));
+    if constexpr (!Regs::kVInK) {
+#pragma unroll
+      for (int i = 0; i < Regs::kV; ++i)
+        R.v[i] = *reinterpret_cast<const u32x4*>(row + (FP8 ? VOFF + i * 64 + g * 16 : (VOFF + i * 32 + g * 8) * 2));
+    }
+  };
+
+  auto compute_tile = [&](const Regs& R, int ti) {
+    const int j0 = start + ti * 16;
+    // V rows of the 16 keys into this wave's LDS tile, as bf16 [key][dim]
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (Regs::kVInK) {
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i)
+        *reinterpret_cast<u32x4*>(vt + n * VP + i * 32 + g * 8) = R.k[VOFF / 32 + i];
+    } else if constexpr (!FP8) {
+#pragma unroll
+      for (int i = 0; i < Regs::kV; ++i) *reinterpret_cast<u32x4*>(vt + n * VP + i * 32 + g * 8) = R.v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < Regs::kV; ++i) {
+        u32x4 lo, hi2;
+        u32x2 t0 = fp8x4_to_bf16x4(R.v[i][0]), t1 = fp8x4_to_bf16x4(R.v[i][1]);
+        u32x2 t2 = fp8x4_to_bf16x4(R.v[i][2]), t3 = fp8x4_to_bf16x4(R.v[i][3]);
+        lo = u32x4{t0[0], t0[1], t1[0], t1[1]};
+        hi2 = u32x4{t2[0], t2[1], t3[0], t3[1]};
+        *reinterpret_cast<u32x4*>(vt + n * VP + i * 64 + g * 16) = lo;
+        *reinterpret_cast<u32x4*>(vt + n * VP + i * 64 + g * 16 + 8) = hi2;
+      }
+    }
+    // S^T = K Q^T
+    f32x4 s[NR];
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) s[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kop;
+      if constexpr (FP8) {
+        const u32x4& w = R.k[ks >> 1];
+        u32x2 c0 = fp8x4_to_bf16x4((ks & 1) ? w[2] : w[0]);
+        u32x2 c1 = fp8x4_to_bf16x4((ks & 1) ? w[3] : w[1]);
+        kop = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
+      } else {
+        kop = __builtin_bit_cast(bf16x8, R.k[ks]);
+      }
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg) s[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[rg][ks], s[rg], 0, 0, 0);
+    }
+    // online softmax; lane holds keys j0+4g+i (i<4) of row rg*16+n
+    s16x4 pb[NR];
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      float x[4];
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * g + i;
+        x[i] = (j <= hi[rg]) ? s[rg][i] * sl2 : kNegInf;
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = max_over_groups(mx);
+      const float mn = fmaxf(m[rg], mx);
+      const float base = (mn == kNegInf) ? 0.f : mn;      // all masked so far: p = 0, no NaN
+      const float alpha = fast_exp2(m[rg] - base);          // m = -inf -> 0
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(x[i] - base);
+        ps += p[i];
+      }
+      l[rg] = l[rg] * alpha + ps;
+      m[rg] = mn;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha;
+      }
+      u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      pb[rg] = __builtin_bit_cast(s16x4, pk);
+    }
+    // O^T += V^T P^T
+    __builtin_amdgcn_wave_barrier();
+    const int tr_row = 4 * g + (n >> 2), tr_col = 4 * (n & 3);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vt + tr_row * VP + db * 16 + tr_col));
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg)
+        acc[rg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb[rg], acc[rg][db], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: this wave's tiles wave, wave+NW, ... with 2 register buffers ----
+  {
+    Regs b0, b1;
+    int ti = wave;
+    if (ti < nt) load_tile(b0, ti);
+    while (ti < nt) {
+      const int t1 = ti + NW;
+      if (t1 < nt) load_tile(b1, t1);
+      compute_tile(b0, ti);
+      if (t1 >= nt) break;
+      const int t2 = t1 + NW;
+      if (t2 < nt) load_tile(b0, t2);
+      compute_tile(b1, t1);
+      ti = t2;
+    }
+  }
+
+  // ---- merge the NW waves' states through LDS, fixed order ----
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) l[rg] = sum_over_groups(l[rg]);
+  __syncthreads();                                   // V tiles are dead from here on
+  float* mw = reinterpret_cast<float*>(smem);        // [NW][ROWS]
+  float* lw = mw + NW * ROWS;                        // [NW][ROWS]
+  float* buf = lw + NW * ROWS;                       // [ROWS][MERGE_PITCH]
+  if (g == 0) {
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg) {
+      mw[wave * ROWS + rg * 16 + n] = m[rg];
+      lw[wave * ROWS + rg * 16 + n] = l[rg];
+    }
+  }
+  __syncthreads();
+  float f[NR];
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    const int r = rg * 16 + n;
+    float M = kNegInf;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * ROWS + r]);
+    float Ls = 0.f;
+    if (M != kNegInf)
+      for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
+    f[rg] = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m[rg] - M) / Ls * vscale;
+  }
+  for (int w = 0; w < NW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rg = 0; rg < NR; ++rg) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          f32x4* dst = reinterpret_cast<f32x4*>(buf + (rg * 16 + n) * MERGE_PITCH + db * 16 + 4 * g);
+          const f32x4 v = acc[rg][db] * f[rg];
+          if (w == 0) *dst = v;
+          else *dst = *dst + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- write partials: rows that are live query rows of this sequence ----
+  const int64_t Hq = a.num_q_heads;
+  for (int idx = threadIdx.x; idx < ROWS * (DV / 4); idx += NW * 64) {
+    const int r = idx / (DV / 4), c4 = idx - r * (DV / 4);
+    const int qi = r / G, hh = r - qi * G;
+    if (qi >= L || qi >= a.max_q) continue;
+    const int64_t tok = q0 + qi, head = kvh * G + hh;
+    float* dst = a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4;
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(buf + r * MERGE_PITCH + c4 * 4);
+  }
+  if (threadIdx.x < ROWS) {
+    const int r = threadIdx.x;
+    const int qi = r / G, hh = r - qi * G;
+    if (qi < L && qi < a.max_q) {
+      float M = kNegInf, Ls = 0.f;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * ROWS + r]);
+      if (M != kNegInf)
+        for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
+      const float lse = (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2;
+      const int64_t tok = q0 + qi, head = kvh * G + hh;
+      a.part_lse[(tok * Hq + head) * P + part] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one workgroup per (row, head); w_p = exp(lse_p - M), out = sum w o / sum w
+// (diffbot model card, "Update 2026-10-01": all-empty rows give 0, not NaN).
+template <int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
+  extern __shared__ float wsh[];                     // [P] weights
+  __shared__ float red[NT / 64];
+  const int64_t rh = blockIdx.x;                     // row * Hq + head
+  const int P = a.num_partitions, DV = a.dv;
+  const float* lse = a.part_lse + rh * P;
+  float mx = kNegInf;
+  for (int p = threadIdx.x; p < P; p += NT) mx = fmaxf(mx, lse[p]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  float M = kNegInf;
+  for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int p = threadIdx.x; p < P; p += NT) {
+    const float w = (M == kNegInf) ? 0.f : __expf(lse[p] - M);
+    wsh[p] = w;
+    sum += w;
+  }
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < NT / 64; ++w) tot += red[w];
+  const float inv = (M == kNegInf || tot == 0.f) ? 0.f : 1.0f / tot;
+  const float* po = a.part_out + rh * P * DV;
+  uint16_t* out = a.out + rh * DV;
+  for (int d = threadIdx.x; d < DV; d += NT) {
+    float accv = 0.f;
+    for (int p = 0; p < P; ++p) accv += wsh[p] * po[(int64_t)p * DV + d];
+    bf16x2 r;
+    r[0] = (__bf16)(accv * inv);
+    out[d] = __builtin_bit_cast(uint16_t, r[0]);
+  }
+  if (a.out_lse && threadIdx.x == 0) a.out_lse[rh] = (M == kNegInf || tot == 0.f) ? kNegInf : M + __logf(tot);
+}
+
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int VOFF, int NR, bool FP8>
+static void launch_one(const SplitArgs& a, hipStream_t s) {
+  constexpr int NW = 4;
+  dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(NW * 64);
+  hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW>), grid, block, 0, s, a);
+}
+
+static int rows_groups(const SplitArgs& a) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const int rows = a.max_q * G;
+  return rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : 0;
+}
+
+bool splitkv_supported(const SplitArgs& a) {
+  const int nr = rows_groups(a);
+  if (nr == 0) return false;
+  const bool fp8 = a.c.esize == 1;
+  if (a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192) return true;
+  if (a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0 && !fp8 && nr == 1) return true;
+  return false;
+}
+
+bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
+  const int nr = rows_groups(a);
+  const bool fp8 = a.c.esize == 1;
+  if (a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192) {
+    if (fp8) {
+      if (nr == 1) launch_one<192, 128, 192, 1, true>(a, s);
+      else if (nr == 2) launch_one<192, 128, 192, 2, true>(a, s);
+      else launch_one<192, 128, 192, 4, true>(a, s);
+    } else {
+      if (nr == 1) launch_one<192, 128, 192, 1, false>(a, s);
+      else if (nr == 2) launch_one<192, 128, 192, 2, false>(a, s);
+      else launch_one<192, 128, 192, 4, false>(a, s);
+    }
+    return true;
+  }
+  if (a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0 && !fp8 && nr == 1) {
+    launch_one<576, 512, 0, 1, false>(a, s);
+    return true;
+  }
+  return false;
+}
+
+bool launch_merge(const MergeArgs& a, hipStream_t s) {
+  constexpr int NT = 128;
+  const int64_t n = (int64_t)a.rows * a.num_q_heads;
+  if (n == 0) return true;
+  hipLaunchKernelGGL((merge_kernel<NT>), dim3((unsigned)n), dim3(NT), a.num_partitions * sizeof(float), s, a);
+  return true;
+}
+
+}  // namespace pa

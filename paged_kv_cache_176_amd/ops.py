@@ -1,0 +1,269 @@
+"""ctypes binding of the C ABI in ``include/pagedattn.h`` (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+_lib = None
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
+_STATUS = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_HIP"}
+KV_BF16, KV_FP8 = 0, 1
+SCALE_NONE, SCALE_TENSOR, SCALE_HEAD = 0, 1, 2
+EXPORTS = ("attn_cache_write", "attn_splitkv_workspace_bytes", "attn_decode_splitkv", "attn_merge_lse",
+           "attn_prefill_causal", "attn_verify", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _CacheDescC(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("row_dim", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("v_offset", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("stride_block", ctypes.c_int64),
+        ("stride_slot", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("dtype", ctypes.c_int),
+        ("scale_mode", ctypes.c_int),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: Optional[str] = None):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with paged_kv_cache_176_amd/build.py (no fallback exists)")
+    lib = ctypes.CDLL(p)
+    i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(_CacheDescC)
+    lib.attn_cache_write.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, dp, vp]
+    lib.attn_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_splitkv_workspace_bytes.restype = sz
+    lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp]
+    lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
+    for name in ("attn_cache_write", "attn_decode_splitkv", "attn_merge_lse", "attn_prefill_causal", "attn_verify"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != ATTN_OK:
+        raise AttnError(st, _lib.attn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class CacheDesc:
+    """A paged KV cache living in ``storage`` (any dtype; addressed by element strides).
+
+    Element (block, slot, head, col) is at storage_base + block*stride_block +
+    slot*stride_slot + head*stride_head + col, in cache elements (2 bytes for
+    bf16, 1 byte for fp8).
+    """
+    storage: torch.Tensor
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    row_dim: int
+    head_dim_k: int
+    head_dim_v: int
+    v_offset: int
+    kv_dtype: str = "bf16"
+    stride_block: Optional[int] = None
+    stride_slot: Optional[int] = None
+    stride_head: Optional[int] = None
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+    scale_mode: str = "none"
+
+    def __post_init__(self):
+        if self.stride_head is None:
+            self.stride_head = self.row_dim
+        if self.stride_slot is None:
+            self.stride_slot = self.num_kv_heads * self.stride_head
+        if self.stride_block is None:
+            self.stride_block = self.block_size * self.stride_slot
+
+    @classmethod
+    def from_geom(cls, storage, geom, k_scale=None, v_scale=None, scale_mode="none"):
+        return cls(storage, geom.num_blocks, geom.block_size, geom.num_kv_heads, geom.row_dim, geom.head_dim_k,
+                   geom.head_dim_v, geom.v_offset, geom.kv_dtype, geom.stride_block, geom.stride_slot,
+                   geom.stride_head, k_scale, v_scale, scale_mode)
+
+    def c_struct(self) -> _CacheDescC:
+        mode = {"none": SCALE_NONE, "tensor": SCALE_TENSOR, "head": SCALE_HEAD}[self.scale_mode]
+        return _CacheDescC(
+            self.storage.data_ptr(), self.num_blocks, self.block_size, self.num_kv_heads, self.row_dim,
+            self.head_dim_k, self.head_dim_v, self.v_offset, 0, self.stride_block, self.stride_slot,
+            self.stride_head, KV_FP8 if self.kv_dtype == "fp8" else KV_BF16, mode,
+            None if self.k_scale is None else self.k_scale.data_ptr(),
+            None if self.v_scale is None else self.v_scale.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be on the GPU")
+
+
+def cache_write(key: torch.Tensor, value: Optional[torch.Tensor], slot_mapping: torch.Tensor, cache: CacheDesc,
+                stream=None) -> None:
+    """Write key [T, Hkv, Dk] / value [T, Hkv, Dv] (bf16, any token/head strides) into ``cache``."""
+    load_library()
+    _need(key, torch.bfloat16, "key")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    if value is not None:
+        _need(value, torch.bfloat16, "value")
+    if key.stride(-1) != 1 or (value is not None and value.stride(-1) != 1):
+        raise ValueError("the last dim of key/value must be contiguous")
+    d = cache.c_struct()
+    _check(_lib.attn_cache_write(
+        _ptr(key), key.stride(0), key.stride(1),
+        _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
+        _ptr(slot_mapping), key.shape[0], ctypes.byref(d), _stream(stream)))
+
+
+def splitkv_workspace_bytes(rows: int, num_q_heads: int, head_dim_v: int, num_partitions: int) -> int:
+    load_library()
+    return int(_lib.attn_splitkv_workspace_bytes(rows, num_q_heads, head_dim_v, num_partitions))
+
+
+def workspace_views(ws: torch.Tensor, rows, num_q_heads, head_dim_v, P):
+    """(part_out [rows, Hq, P, Dv], part_lse [rows, Hq, P]) fp32 views of a split-KV workspace."""
+    n_out = rows * num_q_heads * P * head_dim_v
+    part_bytes = (n_out * 4 + 255) // 256 * 256
+    f = ws.view(torch.float32)
+    po = f[:n_out].view(rows, num_q_heads, P, head_dim_v)
+    pl = f[part_bytes // 4: part_bytes // 4 + rows * num_q_heads * P].view(rows, num_q_heads, P)
+    return po, pl
+
+
+def _workspace(rows, hq, dv, P, device, ws):
+    need = splitkv_workspace_bytes(rows, hq, dv, P)
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws
+
+
+def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                   softmax_scale: float, num_partitions: int, out: Optional[torch.Tensor] = None,
+                   out_lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   partials_only: bool = False, with_lse: bool = True, stream=None):
+    """One query per sequence: q [B, Hq, Dk] bf16 -> (out [B, Hq, Dv] bf16, lse [B, Hq] fp32, workspace)."""
+    load_library()
+    _need(q, torch.bfloat16, "q")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq = q.shape[0], q.shape[1]
+    ws = _workspace(B, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
+    if not partials_only and out is None:
+        out = torch.empty(B, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
+    if not partials_only and with_lse and out_lse is None:
+        out_lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    d = cache.c_struct()
+    _check(_lib.attn_decode_splitkv(
+        _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
+        _ptr(seq_lens), float(softmax_scale), num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+    return out, out_lse, ws
+
+
+def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torch.Tensor] = None,
+              out_lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
+    """part_out [rows, Hq, P, Dv] fp32, part_lse [rows, Hq, P] fp32 -> (out bf16, lse fp32)."""
+    load_library()
+    _need(part_out, torch.float32, "part_out")
+    _need(part_lse, torch.float32, "part_lse")
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    rows, Hq, P, Dv = part_out.shape
+    if out is None:
+        out = torch.empty(rows, Hq, Dv, dtype=torch.bfloat16, device=part_out.device)
+    if with_lse and out_lse is None:
+        out_lse = torch.empty(rows, Hq, dtype=torch.float32, device=part_out.device)
+    _check(_lib.attn_merge_lse(_ptr(part_out), _ptr(part_lse), rows, Hq, Dv, P, _ptr(out), _ptr(out_lse),
+                               _stream(stream)))
+    return out, out_lse
+
+
+def prefill_causal(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                   block_tables: torch.Tensor, cache: CacheDesc, softmax_scale: float, max_query_len: int,
+                   out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                   with_lse: bool = True, stream=None):
+    load_library()
+    _need(q, torch.bfloat16, "q")
+    T, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty(T, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
+    if with_lse and out_lse is None:
+        out_lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
+    d = cache.c_struct()
+    _check(_lib.attn_prefill_causal(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
+        ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
+        _ptr(out), _ptr(out_lse), _stream(stream)))
+    return out, out_lse
+
+
+def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
+           cache: CacheDesc, softmax_scale: float, max_query_len: int, num_partitions: int,
+           out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, partials_only: bool = False, with_lse: bool = True,
+           stream=None):
+    load_library()
+    _need(q, torch.bfloat16, "q")
+    T, Hq = q.shape[0], q.shape[1]
+    ws = _workspace(T, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
+    if not partials_only and out is None:
+        out = torch.empty(T, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
+    if not partials_only and with_lse and out_lse is None:
+        out_lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
+    d = cache.c_struct()
+    _check(_lib.attn_verify(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
+        ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
+        num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+    return out, out_lse, ws

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every entry point the header declares, and
+rejects bad host-side arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_176_amd as pk
+from paged_kv_cache_176_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pk.library_path()):
+        pytest.fail("libpagedattn.so is not built (run __graft_entry__.build())")
+    return pk.load_library()
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("attn_cache_write", "attn_decode_splitkv", "attn_merge_lse", "attn_prefill_causal", "attn_verify"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pk.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(ops.EXPORTS) == set(declared_functions())
+
+
+def test_struct_layout_matches_header(lib):
+    # data(8) + 8 x int32(32) + 3 x int64(24) + 2 x enum(8) + 2 pointers(16)
+    assert ctypes.sizeof(ops._CacheDescC) == 88
+    assert ops._CacheDescC.stride_block.offset == 40
+    assert ops._CacheDescC.k_scale.offset == 72
+
+
+def _desc(**kw):
+    base = dict(data=0x1000, num_blocks=4, block_size=16, num_kv_heads=4, row_dim=320, head_dim_k=192,
+                head_dim_v=128, v_offset=192, reserved0=0, stride_block=16 * 4 * 320, stride_slot=4 * 320,
+                stride_head=320, dtype=0, scale_mode=0, k_scale=None, v_scale=None)
+    base.update(kw)
+    return ops._CacheDescC(**base)
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(data=None), "data is NULL"),
+    (dict(num_blocks=0), "must be positive"),
+    (dict(v_offset=200), "does not fit"),
+    (dict(head_dim_k=400), "does not fit"),
+    (dict(stride_head=100), "strides"),
+    (dict(dtype=1, scale_mode=0), "fp8 caches need"),
+    (dict(dtype=7), "unknown cache dtype"),
+])
+def test_cache_write_rejects_bad_descriptors(lib, bad, msg):
+    d = _desc(**bad)
+    st = lib.attn_cache_write(ctypes.c_void_p(0x2000), 768, 192, None, 0, 0, ctypes.c_void_p(0x3000), 3,
+                              ctypes.byref(d), None)
+    assert st == ops.ATTN_E_INVALID
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_zero_tokens_is_a_noop_and_null_desc_is_invalid(lib):
+    d = _desc()
+    assert lib.attn_cache_write(None, 0, 0, None, 0, 0, None, 0, ctypes.byref(d), None) == ops.ATTN_OK
+    assert lib.attn_cache_write(None, 0, 0, None, 0, 0, None, 1, None, None) == ops.ATTN_E_INVALID
+
+
+def test_splitkv_argument_checks(lib):
+    d = _desc()
+    ws_need = lib.attn_splitkv_workspace_bytes(2, 8, 128, 4)
+    assert ws_need >= 2 * 8 * 4 * 129 * 4
+    assert lib.attn_splitkv_workspace_bytes(-1, 8, 128, 4) == 0
+    args = lambda P, ws_bytes, hq=8: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, hq, ctypes.byref(d),
+                                      ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
+                                      ctypes.c_void_p(0x40000), ws_bytes, ctypes.c_void_p(0x50000), None, None)
+    assert lib.attn_decode_splitkv(*args(0, ws_need)) == ops.ATTN_E_INVALID
+    assert lib.attn_decode_splitkv(*args(5000, ws_need)) == ops.ATTN_E_INVALID
+    assert lib.attn_decode_splitkv(*args(4, ws_need - 1)) == ops.ATTN_E_INVALID
+    assert "workspace" in lib.attn_last_error().decode()
+    assert lib.attn_decode_splitkv(*args(4, ws_need, hq=6)) == ops.ATTN_E_INVALID   # 6 % 4 != 0
+    # a head-dim pair without a kernel is UNSUPPORTED, not INVALID
+    d2 = _desc(head_dim_k=64, head_dim_v=64, v_offset=64, row_dim=128, stride_head=128,
+               stride_slot=512, stride_block=16 * 512)
+    a = list(args(4, ws_need))
+    a[5] = ctypes.byref(d2)
+    assert lib.attn_decode_splitkv(*a) == ops.ATTN_E_UNSUPPORTED
+
+
+def test_merge_and_prefill_argument_checks(lib):
+    assert lib.attn_merge_lse(None, None, 1, 8, 128, 4, None, None, None) == ops.ATTN_E_INVALID
+    assert lib.attn_merge_lse(None, None, 0, 8, 128, 4, None, None, None) == ops.ATTN_OK
+    assert lib.attn_merge_lse(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 1, 8, 128, 5000,
+                              ctypes.c_void_p(1 << 22), None, None) == ops.ATTN_E_UNSUPPORTED
+    d = _desc()
+    st = lib.attn_prefill_causal(None, 0, 0, None, 1, 4, 4, 8, ctypes.byref(d), None, 1, None, 0.1, None, None, None)
+    assert st == ops.ATTN_E_INVALID
+    st = lib.attn_prefill_causal(ctypes.c_void_p(0x1000), 8 * 192, 192, ctypes.c_void_p(0x2000), 1, 4, 4, 8,
+                                 ctypes.byref(d), ctypes.c_void_p(0x3000), 1, ctypes.c_void_p(0x4000),
+                                 float("nan"), ctypes.c_void_p(0x5000), None, None)
+    assert st == ops.ATTN_E_INVALID and "not finite" in lib.attn_last_error().decode()
+
+
+def test_version_string(lib):
+    assert lib.attn_version().decode().startswith("pagedattn")
