@@ -1,0 +1,305 @@
+"""Throughput of the paged-KV attention hot path on one MI355X.
+
+A step is one decode pass of the long-context configuration (batch 1, 131072
+keys, 32 query heads over 4 KV heads, K192/V128 bf16, block size 16):
+  1. attn_cache_write of each sequence's new token (its K/V row),
+  2. the split-KV partial kernel over the whole paged context,
+  3. attn_merge_lse into the bf16 output.
+Inputs are resident in HBM before the timed region.  The step rotates over
+several identical cache copies totalling >= 1 GB, so no step finds its K/V in
+the 256 MB MALL left behind by the previous one.
+
+value = algorithmic bytes per step / step time, where the algorithmic bytes are
+the K/V rows read once per (sequence, KV head) plus Q, O and the block table.
+The "roofline" object reports the split-KV partial kernel alone (HIP events on
+the launch stream) against the 8 TB/s HBM peak; the oracle is timed on the
+host's cores as a reported baseline.  Secondary lines (other decode shapes,
+fp8 verify, MLA decode, chunked-prefill TFLOP/s) are printed under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+MALL_BYTES = 256 << 20
+
+
+def _copies(nbytes):
+    return max(4, math.ceil((1 << 30) / max(1, nbytes)))
+
+
+def auto_partitions(batch, kv_heads, ctx, target_wgs=1024, min_keys=256):
+    """Split count: enough workgroups to fill 256 CUs, partitions of >= min_keys keys."""
+    p = max(1, math.ceil(target_wgs / max(1, batch * kv_heads)))
+    p = min(p, max(1, ctx // min_keys), 4096)
+    return p
+
+
+class DecodeCase:
+    """A decode (or MLA decode) workload on the GPU with rotating cache copies."""
+
+    def __init__(self, w, P, dev="cuda:0"):
+        import torch
+        import paged_kv_cache_176_amd as pk
+        import workloads
+        self.w, self.P = w, P
+        g = w.geom
+        img = w.cache_init.clone()
+        if "pre_slots" in w.extra:
+            workloads.place_bf16_rows(img, g, w.extra["pre_slots"], w.extra["pre_key"], w.extra["pre_value"])
+        self.cache_cpu = img
+        nbytes = img.numel() * img.element_size()
+        self.ncopy = 1 if nbytes > 4 * MALL_BYTES else _copies(nbytes)
+        self.copies = [img.to(dev) for _ in range(self.ncopy)]
+        self.descs = [pk.CacheDesc.from_geom(s, g) for s in self.copies]
+        self.q = w.q.to(dev)
+        self.key = w.key.to(dev)
+        self.value = w.value.to(dev) if w.value is not None else None
+        self.slots = w.slot_mapping.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.seq_lens = w.seq_lens.to(dev)
+        B, Hq = w.q.shape[0], w.q.shape[1]
+        self.ws = torch.empty(pk.splitkv_workspace_bytes(B, Hq, g.head_dim_v, P), dtype=torch.uint8, device=dev)
+        from paged_kv_cache_176_amd.ops import workspace_views
+        self.po, self.pl = workspace_views(self.ws, B, Hq, g.head_dim_v, P)
+        self.out = torch.empty(B, Hq, g.head_dim_v, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        self.pk = pk
+        kv_row = (g.head_dim_k + (g.head_dim_v if g.v_offset >= g.head_dim_k else 0)) * g.elem_bytes
+        self.kv_bytes = int(w.seq_lens.sum().item()) * g.num_kv_heads * kv_row
+        self.other_bytes = (w.q.numel() * 2 + B * Hq * g.head_dim_v * 2 +
+                            sum(math.ceil(int(s) / g.block_size) for s in w.seq_lens.tolist()) * 4)
+        # flops: QK^T and PV over every visible key of every query head
+        self.flops = 2 * int(w.seq_lens.sum().item()) * Hq * (g.head_dim_k + g.head_dim_v)
+
+    def step(self, i, ev=None):
+        pk = self.pk
+        d = self.descs[i % self.ncopy]
+        pk.cache_write(self.key, self.value, self.slots, d)
+        if ev is not None:
+            ev[0].record()
+        pk.decode_splitkv(self.q, d, self.bt, self.seq_lens, self.w.softmax_scale, self.P, workspace=self.ws,
+                          partials_only=True)
+        if ev is not None:
+            ev[1].record()
+        pk.merge_lse(self.po, self.pl, out=self.out, out_lse=self.lse)
+
+
+def time_steps(fn, steps, warmup, events=False):
+    """Warm up, then time exactly ``steps`` calls between two synchronisations."""
+    import torch
+    for i in range(warmup):
+        fn(i, None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)] \
+        if events else [None] * steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    kern = None
+    if events:
+        kern = sum(a.elapsed_time(b) for a, b in evs) / steps / 1e3
+    return dt, kern
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """Time the fp64 oracle on a bounded sample: whole decode steps of the same workload."""
+    import numpy as np
+    import torch
+    import threadpoolctl
+    from oracle import paged_ref as R
+    import workloads
+    g = w.geom
+    img = w.cache_init.clone()
+    spec = R.CacheSpec.from_geom(g)
+    if "pre_slots" in w.extra:
+        workloads.place_bf16_rows(img, g, w.extra["pre_slots"], w.extra["pre_key"], w.extra["pre_value"])
+    base = img.numpy().view(np.uint16)
+    kb = w.key.view(torch.int16).numpy().view(np.uint16)
+    vb = w.value.view(torch.int16).numpy().view(np.uint16)
+    qb = w.q.view(torch.int16).numpy().view(np.uint16)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        c = R.cache_write(base, spec, kb, vb, w.slot_mapping.numpy())
+        R.paged_attention(qb, w.query_start_loc.numpy(), w.seq_lens.numpy(), w.block_tables.numpy(), c, spec,
+                          w.softmax_scale)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    blas = [x.get("num_threads", 1) for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
+    cores = max([len(os.sched_getaffinity(0))] + blas) if blas else len(os.sched_getaffinity(0))
+    return dt, n, min(cores, len(os.sched_getaffinity(0)))
+
+
+def run_prefill(steps, warmup):
+    """Chunked prefill of 32768 tokens in 4096-token chunks: write + causal attention per chunk."""
+    import torch
+    import paged_kv_cache_176_amd as pk
+    import workloads
+    w = workloads.prefill_chunks()
+    dev = "cuda:0"
+    st = w.cache_init.to(dev)
+    d = pk.CacheDesc.from_geom(st, w.geom)
+    q, key, val, slots, bt = (w.q.to(dev), w.key.to(dev), w.value.to(dev), w.slot_mapping.to(dev),
+                              w.block_tables.to(dev))
+    C = w.extra["chunk"]
+    T = q.shape[0]
+    out = torch.empty(T, 32, 128, dtype=torch.bfloat16, device=dev)
+    qsl = torch.tensor([0, C], dtype=torch.int32, device=dev)
+    seqs = [torch.tensor([(c + 1) * C], dtype=torch.int32, device=dev) for c in range(T // C)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T // C)]
+    kern = [0.0] * (T // C)
+
+    def one(i, _):
+        for c in range(T // C):
+            sl = slice(c * C, (c + 1) * C)
+            pk.cache_write(key[sl], val[sl], slots[sl], d)
+            ev[c][0].record()
+            pk.prefill_causal(q[sl], qsl, seqs[c], bt, d, w.softmax_scale, C, out=out[sl], with_lse=False)
+            ev[c][1].record()
+
+    dt, _ = time_steps(one, steps, warmup)
+    # per-chunk kernel times from one more instrumented pass
+    one(0, None)
+    torch.cuda.synchronize()
+    kern = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    visible = sum((c * C) * C + C * (C + 1) // 2 for c in range(T // C))     # causal pairs per head
+    flops = 2 * visible * 32 * (192 + 128)
+    return dict(workload="prefill_32768_in_4096_chunks_bs16", ms_per_pass=dt * 1e3, tflops=flops / dt / 1e12,
+                kernel_ms=sum(kern) * 1e3, kernel_tflops=flops / sum(kern) / 1e12,
+                frac_of_bf16_peak=flops / sum(kern) / 1e12 / BF16_PEAK_TFLOPS,
+                per_chunk_kernel_ms=[round(k * 1e3, 4) for k in kern])
+
+
+def run_verify(mode, steps, warmup, P):
+    import torch
+    import paged_kv_cache_176_amd as pk
+    import workloads
+    w = workloads.fp8_verify(scale_mode=mode)
+    dev = "cuda:0"
+    st = w.cache_init.to(dev)
+    ks, vs = w.k_scale.to(dev), w.v_scale.to(dev)
+    d0 = pk.CacheDesc.from_geom(st, w.geom, ks, vs, mode)
+    pk.cache_write(w.key.to(dev), w.value.to(dev), w.slot_mapping.to(dev), d0)
+    torch.cuda.synchronize()
+    nbytes = st.numel()
+    copies = [st] + [st.clone() for _ in range(_copies(nbytes) - 1)]
+    descs = [pk.CacheDesc.from_geom(s, w.geom, ks, vs, mode) for s in copies]
+    q, qsl, sl, bt = w.q.to(dev), w.query_start_loc.to(dev), w.seq_lens.to(dev), w.block_tables.to(dev)
+    T = q.shape[0]
+    ws = torch.empty(pk.splitkv_workspace_bytes(T, 32, 128, P), dtype=torch.uint8, device=dev)
+    out = torch.empty(T, 32, 128, dtype=torch.bfloat16, device=dev)
+
+    def one(i, ev):
+        if ev is not None:
+            ev[0].record()
+        pk.verify(q, qsl, sl, bt, descs[i % len(descs)], w.softmax_scale, w.max_query_len, P, out=out,
+                  workspace=ws, with_lse=False)
+        if ev is not None:
+            ev[1].record()
+
+    dt, kern = time_steps(one, steps, warmup, events=True)
+    kv = 4 * 46080 * 4 * 320
+    return dict(workload=f"fp8_verify_b4_s46080_l4_{mode}", P=P, us_per_call=dt * 1e6, kernel_us=kern * 1e6,
+                kv_gbs=kv / kern / 1e9)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partitions", type=int, default=0, help="split count (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_176_amd as pk
+    import workloads
+    pk.load_library()
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+
+    B, S, BS = 1, 131072, 16
+    P = args.partitions or auto_partitions(B, 4, S)
+    w = workloads.long_decode(B, S, BS)
+    case = DecodeCase(w, P)
+    ev_pair = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    dt, kern = time_steps(case.step, args.steps, args.warmup, events=True)
+    algo = case.kv_bytes + case.other_bytes
+    value = algo / dt / 1e9
+    achieved = case.kv_bytes / kern / 1e9
+    line = {
+        "metric": "decode attn KV-read GB/s (% HBM peak) + prefill TFLOP/s, K192/V128 bf16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode_b{B}_s{S}_bs{BS}", "batch": B, "context": S, "q_heads": 32, "kv_heads": 4,
+                   "head_dim_k": 192, "head_dim_v": 128, "block_size": BS, "partitions": P,
+                   "cache_copies_rotated": case.ncopy, "step": "cache write of the new token + split-KV decode + merge",
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "splitkv_partial_kernel<192,128,192,1,bf16>", "kernel_us": round(kern * 1e6, 3),
+                     "algorithmic_bytes_per_launch": case.kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        cdt, n, cores = cpu_baseline(w)
+        line["cpu_baseline"] = {"value": round(algo / cdt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                                "sample": f"{n} whole decode step(s) of the same workload (cache write + fp64 "
+                                          f"attention over all 131072 keys), {cdt:.2f} s each"}
+    if not args.no_extra:
+        extra = {}
+        for (b2, s2, bs2) in [(1, 131072, 64), (8, 8192, 16), (8, 8192, 64)]:
+            w2 = workloads.long_decode(b2, s2, bs2)
+            p2 = auto_partitions(b2, 4, s2)
+            c2 = DecodeCase(w2, p2)
+            d2, k2 = time_steps(c2.step, 100, 10, events=True)
+            extra[f"decode_b{b2}_s{s2}_bs{bs2}"] = dict(P=p2, us_per_step=round(d2 * 1e6, 2),
+                                                        kernel_us=round(k2 * 1e6, 2),
+                                                        kv_gbs=round(c2.kv_bytes / k2 / 1e9, 1),
+                                                        step_gbs=round((c2.kv_bytes + c2.other_bytes) / d2 / 1e9, 1))
+            del c2
+        for b2, p2 in [(1, 96), (16, 32)]:
+            w2 = workloads.mla_decode(b2, 100000)
+            c2 = DecodeCase(w2, p2)
+            d2, k2 = time_steps(c2.step, 50, 5, events=True)
+            extra[f"mla_b{b2}_s100000_h12"] = dict(P=p2, us_per_step=round(d2 * 1e6, 2), kernel_us=round(k2 * 1e6, 2),
+                                                   kv_gbs=round(c2.kv_bytes / k2 / 1e9, 1),
+                                                   tflops=round(c2.flops / k2 / 1e12, 2))
+            del c2
+        for mode in ("tensor", "head"):
+            extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, 64)
+        extra["prefill"] = run_prefill(5, 2)
+        line["extra"] = extra
+        torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
