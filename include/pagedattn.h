@@ -117,10 +117,11 @@ attn_status attn_cache_write(const void* key, int64_t key_stride_tok, int64_t ke
 /* ---------------------------------------------------------------------------
  * Split-KV workspace.  Partials of `rows` query rows over num_partitions key
  * ranges: part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 (each
- * normalised by its own softmax sum) followed by part_lse [rows, num_q_heads,
- * num_partitions] fp32 (-inf for an empty range), starting at the workspace's
- * first byte, then a small area of per-(row-group) counters.  Returns the bytes
- * needed (0 for invalid arguments).                                            */
+ * normalised by its own softmax sum) at byte 0, then part_lse [rows,
+ * num_q_heads, num_partitions] fp32 (-inf for an empty range) at the next
+ * 256-byte boundary.  Contents need no initialisation.  Two calls that share a
+ * workspace must not run concurrently.  Returns the bytes needed (0 for invalid
+ * arguments).                                                                  */
 size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim_v,
                                     int32_t num_partitions);
 

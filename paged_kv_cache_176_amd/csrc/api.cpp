@@ -80,12 +80,13 @@ attn_status attention_layout_ok(const pa::CacheView& c, const void* q, int64_t q
   return ATTN_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace: part_out | part_lse, each starting on a 256-byte boundary.
 size_t splitkv_bytes(int64_t rows, int64_t hq, int64_t dv, int64_t P) {
   const size_t part = (size_t)(rows * hq * P * dv) * sizeof(float);
   const size_t lse = (size_t)(rows * hq * P) * sizeof(float);
-  const size_t a = (part + 255) / 256 * 256;
-  const size_t b = (lse + 255) / 256 * 256;
-  return a + b + 256;
+  return align256(part) + align256(lse);
 }
 
 attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_sh, const int32_t* qsl,
@@ -124,7 +125,7 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   a.scale = scale;
   a.num_partitions = P;
   a.part_out = static_cast<float*>(ws);
-  const size_t part_bytes = ((size_t)rows * num_q_heads * P * c.dv * sizeof(float) + 255) / 256 * 256;
+  const size_t part_bytes = align256((size_t)rows * num_q_heads * P * c.dv * sizeof(float));
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes);
   a.rows = rows;
   if (!pa::splitkv_supported(a))
@@ -208,6 +209,7 @@ attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t
   if (!part_out || !part_lse || !out) return fail(ATTN_E_INVALID, "%s: NULL pointer", who);
   if (num_partitions > 4096)
     return fail(ATTN_E_UNSUPPORTED, "%s: %d partitions exceed the merge kernel's limit of 4096", who, num_partitions);
+  if (head_dim_v % 4) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim_v must be a multiple of 4", who);
   pa::MergeArgs m{part_out, part_lse, rows, num_q_heads, head_dim_v, num_partitions, static_cast<uint16_t*>(out),
                   out_lse};
   pa::launch_merge(m, static_cast<hipStream_t>(stream));

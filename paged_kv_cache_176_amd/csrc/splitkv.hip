@@ -297,12 +297,18 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per (row, head); w_p = exp(lse_p - M), out = sum w o / sum w
-// (diffbot model card, "Update 2026-10-01": all-empty rows give 0, not NaN).
-template <int NT>
+// Merge (attn_merge_lse, and the second kernel of attn_decode_splitkv / attn_verify).
+// Grid: (row * Hq + head, slice of 4*SLOTS output dims).  The workgroup's threads
+// are SLOTS float4 columns x NG partition groups, so each thread issues all of
+// its P / NG partial loads at once; group sums are combined in LDS in a fixed
+// order.  w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p, lse = M + ln sum w_p;
+// M = -inf (no partition saw a key) gives out = 0, lse = -inf, never NaN.
+template <int NT, int SLOTS>
 __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
+  constexpr int NG = NT / SLOTS;
   extern __shared__ float wsh[];                     // [P] weights
   __shared__ float red[NT / 64];
+  __shared__ f32x4 gs[NG][SLOTS];
   const int64_t rh = blockIdx.x;                     // row * Hq + head
   const int P = a.num_partitions, DV = a.dv;
   const float* lse = a.part_lse + rh * P;
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __syncthreads();
   float sum = 0.f;
   for (int p = threadIdx.x; p < P; p += NT) {
-    const float w = (M == kNegInf) ? 0.f : __expf(lse[p] - M);
+    const float w = (M == kNegInf) ? 0.f : fast_exp2((lse[p] - M) * kLog2e);
     wsh[p] = w;
     sum += w;
   }
@@ -325,26 +331,47 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
-  const float inv = (M == kNegInf || tot == 0.f) ? 0.f : 1.0f / tot;
-  const float* po = a.part_out + rh * P * DV;
-  uint16_t* out = a.out + rh * DV;
-  for (int d = threadIdx.x; d < DV; d += NT) {
-    float accv = 0.f;
-    for (int p = 0; p < P; ++p) accv += wsh[p] * po[(int64_t)p * DV + d];
-    bf16x2 r;
-    r[0] = (__bf16)(accv * inv);
-    out[d] = __builtin_bit_cast(uint16_t, r[0]);
+  const bool empty = (M == kNegInf || tot == 0.f);
+  const int slot = threadIdx.x % SLOTS, grp = threadIdx.x / SLOTS;
+  const int c4 = blockIdx.y * SLOTS + slot;          // float4 column
+  const float* po = a.part_out + rh * P * DV + c4 * 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c4 * 4 < DV) {
+    int p = grp;
+    for (; p + 3 * NG < P; p += 4 * NG) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + NG) * DV);
+      const f32x4 v2 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + 2 * NG) * DV);
+      const f32x4 v3 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + 3 * NG) * DV);
+      acc += v0 * wsh[p] + v1 * wsh[p + NG] + v2 * wsh[p + 2 * NG] + v3 * wsh[p + 3 * NG];
+    }
+    for (; p < P; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
   }
-  if (a.out_lse && threadIdx.x == 0) a.out_lse[rh] = (M == kNegInf || tot == 0.f) ? kNegInf : M + __logf(tot);
+  gs[grp][slot] = acc;
+  __syncthreads();
+  if (threadIdx.x < SLOTS && c4 * 4 < DV) {
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int g2 = 0; g2 < NG; ++g2) t += gs[g2][slot];
+    t *= empty ? 0.f : 1.0f / tot;
+    u32x2 pk = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+    *reinterpret_cast<u32x2*>(a.out + rh * DV + c4 * 4) = pk;
+  }
+  if (a.out_lse && blockIdx.y == 0 && threadIdx.x == 0) a.out_lse[rh] = empty ? kNegInf : M + __builtin_logf(tot);
 }
 
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int VOFF, int NR, bool FP8>
-static void launch_one(const SplitArgs& a, hipStream_t s) {
-  constexpr int NW = 4;
-  dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(NW * 64);
-  hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW>), grid, block, 0, s, a);
-}
+template <int DK, int DV, int VOFF, int NR, bool FP8, int NW>
+struct SplitKernel {
+  static constexpr int kRows = NR * 16;
+  static constexpr int kVTile = 16 * (DV + 16);
+  static constexpr int kLdsV = NW * kVTile * 2;
+  static constexpr int kLdsM = NW * kRows * 2 * 4 + kRows * (DV + 4) * 4;
+  static constexpr int kLds = kLdsV > kLdsM ? kLdsV : kLdsM;
+  static void launch(const SplitArgs& a, hipStream_t s) {
+    dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(NW * 64);
+    hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW>), grid, block, 0, s, a);
+  }
+};
 
 static int rows_groups(const SplitArgs& a) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
@@ -352,42 +379,49 @@ static int rows_groups(const SplitArgs& a) {
   return rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : 0;
 }
 
-bool splitkv_supported(const SplitArgs& a) {
-  const int nr = rows_groups(a);
-  if (nr == 0) return false;
-  const bool fp8 = a.c.esize == 1;
-  if (a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192) return true;
-  if (a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0 && !fp8 && nr == 1) return true;
-  return false;
-}
+static bool is_diffkv(const SplitArgs& a) { return a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192; }
+static bool is_mla(const SplitArgs& a) { return a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0 && a.c.esize == 2; }
 
-bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
+// Dispatch on (layout, dtype, row groups); F is called with the kernel type.
+template <typename F>
+static bool dispatch(const SplitArgs& a, F&& f) {
   const int nr = rows_groups(a);
   const bool fp8 = a.c.esize == 1;
-  if (a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192) {
+  if (nr == 0) return false;
+  if (is_diffkv(a)) {
     if (fp8) {
-      if (nr == 1) launch_one<192, 128, 192, 1, true>(a, s);
-      else if (nr == 2) launch_one<192, 128, 192, 2, true>(a, s);
-      else launch_one<192, 128, 192, 4, true>(a, s);
+      if (nr == 1) f(SplitKernel<192, 128, 192, 1, true, 4>{});
+      else if (nr == 2) f(SplitKernel<192, 128, 192, 2, true, 4>{});
+      else f(SplitKernel<192, 128, 192, 4, true, 4>{});
     } else {
-      if (nr == 1) launch_one<192, 128, 192, 1, false>(a, s);
-      else if (nr == 2) launch_one<192, 128, 192, 2, false>(a, s);
-      else launch_one<192, 128, 192, 4, false>(a, s);
+      if (nr == 1) f(SplitKernel<192, 128, 192, 1, false, 4>{});
+      else if (nr == 2) f(SplitKernel<192, 128, 192, 2, false, 4>{});
+      else f(SplitKernel<192, 128, 192, 4, false, 4>{});
     }
     return true;
   }
-  if (a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0 && !fp8 && nr == 1) {
-    launch_one<576, 512, 0, 1, false>(a, s);
+  if (is_mla(a) && nr == 1) {
+    f(SplitKernel<576, 512, 0, 1, false, 4>{});
     return true;
   }
   return false;
 }
 
+bool splitkv_supported(const SplitArgs& a) {
+  return dispatch(a, [](auto) {});
+}
+
+bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
+  return dispatch(a, [&](auto k) { decltype(k)::launch(a, s); });
+}
+
 bool launch_merge(const MergeArgs& a, hipStream_t s) {
-  constexpr int NT = 128;
+  constexpr int NT = 256, SLOTS = 8;
   const int64_t n = (int64_t)a.rows * a.num_q_heads;
   if (n == 0) return true;
-  hipLaunchKernelGGL((merge_kernel<NT>), dim3((unsigned)n), dim3(NT), a.num_partitions * sizeof(float), s, a);
+  const int slices = (a.dv / 4 + SLOTS - 1) / SLOTS;
+  hipLaunchKernelGGL((merge_kernel<NT, SLOTS>), dim3((unsigned)n, slices), dim3(NT),
+                     a.num_partitions * sizeof(float), s, a);
   return true;
 }
 
