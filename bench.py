@@ -33,6 +33,20 @@ BF16_PEAK_TFLOPS = 2516.6
 MALL_BYTES = 256 << 20
 
 
+# HBM bytes per launch of the split-KV kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by a copy of known size), keyed by the sha256 of the kernel source they were
+# taken on: any later change to the kernel reports traffic as null until re-measured.
+MEASURED_TRAFFIC = {
+    "5e10c9edba463d8d": 163990.2 * 1024 * 2 + 2176.6 * 1024,
+}
+
+
+def _kernel_source_hash():
+    import hashlib
+    with open(os.path.join(ROOT, "paged_kv_cache_176_amd", "csrc", "splitkv.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def _copies(nbytes):
     return max(4, math.ceil((1 << 30) / max(1, nbytes)))
 
@@ -228,6 +242,9 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="split count (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
+                         "size that calibrates hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -267,7 +284,8 @@ def main():
                    "cache_copies_rotated": case.ncopy, "step": "cache write of the new token + split-KV partial kernel + merge kernel",
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": MEASURED_TRAFFIC.get(_kernel_source_hash()) if P == 128 else None,
                      "kernel": "splitkv_partial_kernel<192,128,192,1,bf16,4 waves>", "kernel_us": round(kern * 1e6, 3),
                      "algorithmic_bytes_per_launch": case.kv_bytes},
     }
@@ -301,6 +319,14 @@ def main():
         extra["prefill"] = run_prefill(5, 2)
         line["extra"] = extra
         torch.cuda.empty_cache()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = n
     print(json.dumps(line), flush=True)
 
 
