@@ -248,7 +248,14 @@ bool prefill_supported(const PrefillArgs& a) {
   return a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192;
 }
 
+bool prefill_fast_eligible(const PrefillArgs& a);
+void launch_prefill_fast(const PrefillArgs& a, hipStream_t s);
+
 bool launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  if (prefill_fast_eligible(a)) {
+    launch_prefill_fast(a, s);
+    return true;
+  }
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int QT = 4 * (64 / G);
   const int tiles = (a.max_q + QT - 1) / QT;
@@ -257,6 +264,296 @@ bool launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.c.esize == 1) hipLaunchKernelGGL((prefill_kernel<192, 128, 192, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((prefill_kernel<192, 128, 192, false>), grid, block, 0, s, a);
   return true;
+}
+
+// ===========================================================================
+// Fast path: bf16 DiffKV rows (K 192 / V 128), block size a multiple of 16.
+//
+//   rows      wave = 64 rows = 2 groups of 32 for v_mfma_f32_32x32x16_bf16; the
+//             32x32 output gives a lane 16 keys of one row, so a row max needs a
+//             single cross-lane step (lanes l and l^32).
+//   K/V       32-key stages land in LDS straight from HBM/L2 with
+//             global_load_lds_dwordx4 (16 B per lane at base + 16*lane): no VGPR
+//             staging.  A 6-stage ring keeps four stages (80 KB) in flight while one
+//             is consumed, enough to cover L2/MALL latency at ~1 us per step;
+//             completion is tracked with explicit vmcnt waits (the compiler does
+//             not track LDS-DMA writes) and one s_barrier per step.  The kernel
+//             must not spill: a scratch reload is a vector-memory op issued after
+//             the DMA, so waiting for it would drain the whole ring.
+//             Slots are XOR-swizzled so the K operand reads (ds_read_b128) and
+//             the transposing V reads (ds_read_b64_tr_b16) are bank-conflict free.
+//   softmax   lazy rescaling: the running max used for exp2 is only moved when
+//             the true max exceeds it by more than 8 (in log2 units), so p <= 256
+//             and the accumulator is rescaled rarely.
+//   order     workgroups of one KV head stay on the same XCDs (they share the
+//             K/V prefix in that XCD's L2); heaviest query tiles first.
+namespace pf {
+constexpr int DK = 192, DV = 128, VOFF = 192;
+constexpr int KT = 32;                   // keys per stage
+constexpr int NSTAGE = 6;                // ring: one stage consumed, up to four in flight
+constexpr int NW = 4;
+constexpr int KCH = DK * 2 / 16;         // 24 chunks of 16 B per K row
+constexpr int VCH = DV * 2 / 16;         // 16 chunks per V row
+constexpr int KSLOTS = KT * KCH;         // 768
+constexpr int SLOTS = KT * (KCH + VCH);  // 1280
+constexpr int PER_WAVE = SLOTS / 64 / NW;  // 5 DMA instructions per wave per stage
+constexpr int STAGE_BYTES = SLOTS * 16;  // 20 KB
+constexpr int BT_MAX = 4096;             // block-table entries staged in LDS
+constexpr int KS = DK / 16;              // 12 k-steps
+constexpr int DB = DV / 32;              // 4 output dim blocks
+}  // namespace pf
+
+__device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ ((key >> 1) & 7)); }
+__device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ ((key & 7) << 1)); }
+
+#define PF_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+__device__ __forceinline__ void pf_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void prefill_fast_kernel(PrefillArgs a, int ntile_max) {
+  using namespace pf;
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE_BYTES];
+  __shared__ int btl[BT_MAX];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int Hkv = a.c.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int TPW = 64 / G;                       // query tokens per wave
+  const int QT = NW * TPW;                      // query tokens per workgroup
+  // ---- workgroup -> (sequence, KV head, tile): XCD-aware, heaviest first ----
+  const int NH = a.num_seqs * Hkv;
+  const int lin = blockIdx.x;
+  int hg, rank;
+  if (NH < 8 && 8 % NH == 0) {
+    const int per = 8 / NH, xcd = lin & 7;
+    hg = xcd / per;
+    rank = (lin >> 3) * per + xcd % per;
+  } else {
+    hg = lin % NH;
+    rank = lin / NH;
+  }
+  const int b = hg / Hkv, kvh = hg - b * Hkv;
+  const int q0 = a.qsl[b];
+  const int L = a.qsl[b + 1] - q0;
+  const int S = a.seq_lens[b];
+  const int ntile = ceil_div(L, QT);
+  if (rank >= ntile) return;
+  const int tile = ntile - 1 - rank;
+  const int off = S - L;
+  const int wt0 = tile * QT + wave * TPW;
+  const int wg_last_q = min(tile * QT + QT, L) - 1;
+  const int wg_hi = min(off + wg_last_q, S - 1);
+  const int nsteps = wg_hi >= 0 ? wg_hi / KT + 1 : 0;
+  const int BS = a.c.block_size;
+  const int nblk = wg_hi >= 0 ? wg_hi / BS + 1 : 0;
+  const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+  for (int i = threadIdx.x; i < nblk; i += 256) btl[i] = btrow[i];
+
+  // ---- Q rows of this wave into registers (B operand), visibility limits ----
+  bf16x8 qreg[2][KS];
+  int hi[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int r = rg * 32 + n32;
+    const int qi = wt0 + r / G, hh = r % G;
+    const bool live = qi < L;
+    hi[rg] = live ? min(off + qi, S - 1) : -1;
+    const uint16_t* qp = a.q + (int64_t)(q0 + (live ? qi : 0)) * a.q_st + (int64_t)(kvh * G + hh) * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = {0, 0, 0, 0};
+      if (live) w = *reinterpret_cast<const u32x4*>(qp + ks * 16 + g * 8);
+      qreg[rg][ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int wave_last_q = min(wt0 + TPW, L) - 1;
+  const int wave_hi = wave_last_q >= wt0 ? min(off + wave_last_q, S - 1) : -1;
+  const int wave_lo = off + wt0;                // keys <= wave_lo are visible to every live row
+  const float sl2 = a.scale * kLog2e;
+  __syncthreads();                              // block table staged; Q loads retired
+
+  auto issue = [&](int st) {
+    char* buf = smem + (st % NSTAGE) * STAGE_BYTES;
+    const int j0 = st * KT;
+    // keys past the workgroup's last visible key re-read that key: every block id used
+    // comes from the staged part of the table (entries 0 .. wg_hi / BS)
+    const int kmax = wg_hi - j0;
+    const int64_t B0 = btl[j0 / BS];
+    const int64_t B1 = btl[min(j0 + 16, wg_hi) / BS];
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int i = wave * PER_WAVE + u;
+      const int slot = i * 64 + lane;
+      int key, byte;
+      if (slot < KSLOTS) {
+        key = slot / KCH;
+        byte = ((slot - key * KCH) ^ ((key >> 1) & 7)) * 16;
+      } else {
+        const int vs = slot - KSLOTS;
+        key = vs / VCH;
+        byte = VOFF * 2 + ((vs - key * VCH) ^ ((key & 7) << 1)) * 16;
+      }
+      const int kc = min(key, kmax);
+      const int64_t blk = kc < 16 ? B0 : B1;
+      const int64_t pos = (j0 + kc) % BS;
+      const uint8_t* src = a.c.data + (blk * a.c.sb + pos * a.c.ss + (int64_t)kvh * a.c.sh) * 2 + byte;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, 0);
+    }
+  };
+
+  auto qk = [&](int st, f32x16 (&s)[2]) {
+    const char* buf = smem + (st % NSTAGE) * STAGE_BYTES;
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[rg][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + pf_k_slot(n32, 2 * ks + g) * 16);
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) s[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rg][ks], s[rg], 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[2][DB];
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rg][db][i] = 0.f;
+
+  auto softmax_pv = [&](int j, const f32x16 (&s)[2]) {
+    const bool need_mask = j * KT + KT - 1 > wave_lo;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      float x[16];
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = s[rg][i] * sl2;
+        if (need_mask) {
+          const int key = j * KT + 8 * (i >> 2) + 4 * g + (i & 3);
+          v = key <= hi[rg] ? v : kNegInf;
+        }
+        x[i] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m[rg], mx);
+      const bool grow = mn > m[rg] + 8.0f;       // true on the first visible key (m = -inf)
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2(m[rg] - mn) : 1.0f;
+        m[rg] = grow ? mn : m[rg];
+        l[rg] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha;
+      }
+      const float base = m[rg] == kNegInf ? 0.f : m[rg];
+      float ps = 0.f;
+      uint32_t pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(x[2 * i] - base), p1 = fast_exp2(x[2 * i + 1] - base);
+        ps += p0 + p1;
+        pk[i] = pack_bf16x2(p0, p1);
+      }
+      l[rg] += ps;
+      pb[rg][0] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      pb[rg][1] = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+    }
+    // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] P^T[16 keys x 32 rows]; the lane's
+    // k order (keys 16kh+4g+0..3, then 16kh+8+4g+0..3) matches its own probabilities
+    const char* buf = smem + (j % NSTAGE) * STAGE_BYTES;
+    const int s16 = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int key0 = 16 * kh + 4 * g + (s16 >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int dim = db * 32 + 16 * half + 4 * (s16 & 3);
+        const int c = dim >> 3, inb = (dim & 7) * 2;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(buf + pf_v_slot(key0, c) * 16 + inb));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(buf + pf_v_slot(key0 + 8, c) * 16 + inb));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+          acc[rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[rg][kh], acc[rg][db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline: stage j is consumed while stages j+1 .. j+NSTAGE-2 are in flight ----
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < nsteps) issue(st);
+  for (int j = 0; j < nsteps; ++j) {
+    const int ahead = min(NSTAGE - 2, nsteps - 1 - j);   // stages issued after stage j
+    if (ahead >= 4) PF_WAIT_VM(20);
+    else if (ahead == 3) PF_WAIT_VM(15);
+    else if (ahead == 2) PF_WAIT_VM(10);
+    else if (ahead == 1) PF_WAIT_VM(5);
+    else PF_WAIT_VM(0);
+    pf_barrier();                                  // stage j resident for all waves; stage j-1 dead
+    if (j + NSTAGE - 1 < nsteps) issue(j + NSTAGE - 1);
+    if (j * KT <= wave_hi) {
+      f32x16 s[2];
+      qk(j, s);
+      softmax_pv(j, s);
+    }
+  }
+
+  // ---- normalise and write ----
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const float lt = l[rg] + __shfl_xor(l[rg], 32, 64);
+    const int r = rg * 32 + n32;
+    const int qi = wt0 + r / G, hh = r % G;
+    if (qi >= L) continue;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int64_t tok = q0 + qi, head = kvh * G + hh;
+    uint16_t* op = a.out + (tok * a.num_q_heads + head) * DV;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        u32x2 pk = {pack_bf16x2(acc[rg][db][4 * qq] * inv, acc[rg][db][4 * qq + 1] * inv),
+                    pack_bf16x2(acc[rg][db][4 * qq + 2] * inv, acc[rg][db][4 * qq + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + db * 32 + 8 * qq + 4 * g) = pk;
+      }
+    if (a.out_lse && g == 0)
+      a.out_lse[tok * a.num_q_heads + head] = lt > 0.f ? (m[rg] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+bool prefill_fast_eligible(const PrefillArgs& a) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  return a.c.esize == 2 && a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192 && a.c.block_size % 16 == 0 &&
+         G >= 1 && 64 % G == 0 && a.bt_stride <= pf::BT_MAX;
+}
+
+void launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const int QT = pf::NW * (64 / G);
+  const int ntile_max = (a.max_q + QT - 1) / QT;
+  const int NH = a.num_seqs * a.c.num_kv_heads;
+  int grid;
+  if (NH < 8 && 8 % NH == 0) {
+    const int per = 8 / NH;
+    grid = (ntile_max + per - 1) / per * per * NH;
+  } else {
+    grid = ntile_max * NH;
+  }
+  if (grid == 0) return;
+  hipLaunchKernelGGL(prefill_fast_kernel, dim3(grid), dim3(256), 0, s, a, ntile_max);
 }
 
 }  // namespace pa

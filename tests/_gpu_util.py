@@ -6,6 +6,10 @@ Tolerances (attention outputs, bf16 vs the fp64 oracle on the SAME cache bytes):
   in both cases also RMSE / RMS(oracle) <= 1e-2 and cosine >= 0.9999, because at long
   context |out| is ~1e-3..1e-2 and an all-zero output would pass the absolute bounds.
 LSE: |lse_gpu - lse_oracle| <= 1e-3 (fp32 log-sum-exp of fp32 scores).
+The absolute bound is applied as stated on the configuration-size tests (strict=True).  On the
+small edge-case tests, whose outputs can be single V rows with |out| > 2.56, the bf16 output's
+own round-to-nearest error (<= 2^-8 |out|) alone can exceed it, so there the bound per element is
+max_abs + 2^-8 |ref|.
 """
 from __future__ import annotations
 
@@ -70,7 +74,7 @@ def oracle_attention(w, cache_np, rows=None):
                              cache_np, R.CacheSpec.from_geom(w.geom), w.softmax_scale, ks, vs, rows=rows)
 
 
-def compare(out_gpu: torch.Tensor, ref: np.ndarray, fp8=False, lse_gpu=None, lse_ref=None, what=""):
+def compare(out_gpu: torch.Tensor, ref: np.ndarray, fp8=False, lse_gpu=None, lse_ref=None, what="", strict=False):
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
@@ -81,7 +85,12 @@ def compare(out_gpu: torch.Tensor, ref: np.ndarray, fp8=False, lse_gpu=None, lse
     cos = float((got * ref).sum() / (np.linalg.norm(got) * np.linalg.norm(ref) + 1e-300)) if err.size else 1.0
     log(f"{what}: max|err| {maxabs:.3e} rmse {rmse:.3e} rel-rmse {rmse / (rms + 1e-300):.3e} cos {cos:.7f} "
         f"rms(ref) {rms:.3e}")
-    assert maxabs <= (5e-2 if fp8 else 1e-2), f"{what}: max abs {maxabs}"
+    bound = 5e-2 if fp8 else 1e-2
+    if strict:
+        assert maxabs <= bound, f"{what}: max abs {maxabs}"
+    else:
+        excess = float((np.abs(err) - 2.0 ** -8 * np.abs(ref)).max()) if err.size else 0.0
+        assert excess <= bound, f"{what}: max abs {maxabs} beyond the bf16 output rounding by {excess}"
     assert rmse <= 1e-3, f"{what}: rmse {rmse}"
     if rms > 0:
         assert rmse / rms <= 1e-2, f"{what}: relative rmse {rmse / rms}"

@@ -28,7 +28,7 @@ def test_tiny_config(gpu_lib, P):
     u.write()
     out, lse, _ = run_decode(u, P)
     ref, ref_lse = oracle_attention(w, u.cache_bytes())
-    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"tiny P={P}")
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"tiny P={P}", strict=True)
 
 
 @pytest.mark.parametrize("lens", [[1], [15, 16, 17], [0, 5, 0], [300, 1, 33], [1000]])
@@ -122,4 +122,4 @@ def test_long_context_config(gpu_lib, shape):
     out, lse, _ = run_decode(u, P)
     log("oracle")
     ref, ref_lse = oracle_attention(w, u.cache_bytes())
-    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"decode B{B} S{S} bs{bs} P{P}")
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"decode B{B} S{S} bs{bs} P{P}", strict=True)

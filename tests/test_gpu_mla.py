@@ -69,4 +69,4 @@ def test_mla_config(gpu_lib, B, P):
     log(f"oracle on seqs {seqs}")
     ref, ref_lse = oracle_attention(w, u.cache_bytes(), rows=seqs)
     idx = torch.tensor(seqs, device=DEV)
-    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what=f"mla B{B} P{P}")
+    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what=f"mla B{B} P{P}", strict=True)

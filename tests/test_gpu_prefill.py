@@ -37,6 +37,20 @@ def test_small_prefill(gpu_lib, kv, case):
     compare(out, ref, fp8=kv != "bf16", lse_gpu=lse, lse_ref=ref_lse, what=f"prefill {case} {kv}")
 
 
+@pytest.mark.parametrize("bs", [8, 64])
+def test_block_sizes_and_batches(gpu_lib, bs):
+    """Block size 8 takes the generic kernel, 64 the LDS-streamed one; several sequences,
+    some queries in the tail of a longer context, one sequence shorter than a tile."""
+    g = workloads.diffkv_geom(0, bs)
+    w = workloads.paged_workload("pf", g, [700, 5, 333, 64], [100, 5, 333, 31], 32, 1 / math.sqrt(192),
+                                 seed=43)
+    u = Uploaded(w)
+    u.write()
+    out, lse = run_prefill(u)
+    ref, ref_lse = oracle_attention(w, u.cache_bytes())
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"prefill bs={bs}")
+
+
 def test_chunked_equals_one_shot(gpu_lib):
     """Prefill in 64-token chunks == one 256-token prefill (bitwise on the shared rows is
     not required: the key tiling differs only by where chunks end)."""
@@ -78,4 +92,4 @@ def test_chunked_prefill_config(gpu_lib):
     log(f"oracle on {len(rows)} rows")
     ref, ref_lse = oracle_attention(w, u.cache_bytes(), rows=rows)
     idx = torch.from_numpy(rows).to(DEV)
-    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what="chunked prefill 32768")
+    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what="chunked prefill 32768", strict=True)

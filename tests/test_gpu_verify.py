@@ -62,7 +62,7 @@ def test_fp8_verify_config(gpu_lib, mode):
     out, lse, _ = run_verify(u, 64)
     log("oracle")
     ref, ref_lse = oracle_attention(w, u.cache_bytes())
-    compare(out, ref, fp8=True, lse_gpu=lse, lse_ref=ref_lse, what=f"fp8 verify {mode}")
+    compare(out, ref, fp8=True, lse_gpu=lse, lse_ref=ref_lse, what=f"fp8 verify {mode}", strict=True)
     tail = out[16:].float().cpu()
     assert torch.all(tail == 0) and not torch.any(torch.signbit(tail))
     assert torch.all(torch.isneginf(lse[16:].cpu()))
