@@ -269,38 +269,42 @@ bool launch_prefill(const PrefillArgs& a, hipStream_t s) {
 // ===========================================================================
 // Fast path: bf16 DiffKV rows (K 192 / V 128), block size a multiple of 16.
 //
-//   rows      wave = 64 rows = 2 groups of 32 for v_mfma_f32_32x32x16_bf16; the
-//             32x32 output gives a lane 16 keys of one row, so a row max needs a
-//             single cross-lane step (lanes l and l^32).
-//   K/V       32-key stages land in LDS straight from HBM/L2 with
+//   rows      workgroup = 8 waves x 32 rows (32 query tokens x 8 GQA heads for G = 8);
+//             a wave's 32 rows are one v_mfma_f32_32x32x16_bf16 column block, whose
+//             output gives a lane 16 keys of one row: a row max needs a single
+//             cross-lane step (lanes l and l^32).  ~200 registers per wave, so two
+//             waves share each SIMD and the hardware overlaps one wave's MFMAs with
+//             the other's softmax.
+//   K/V       64-key stages land in LDS straight from HBM/L2 with
 //             global_load_lds_dwordx4 (16 B per lane at base + 16*lane): no VGPR
-//             staging.  A 6-stage ring keeps four stages (80 KB) in flight while one
-//             is consumed, enough to cover L2/MALL latency at ~1 us per step;
-//             completion is tracked with explicit vmcnt waits (the compiler does
-//             not track LDS-DMA writes) and one s_barrier per step.  The kernel
-//             must not spill: a scratch reload is a vector-memory op issued after
-//             the DMA, so waiting for it would drain the whole ring.
-//             Slots are XOR-swizzled so the K operand reads (ds_read_b128) and
-//             the transposing V reads (ds_read_b64_tr_b16) are bank-conflict free.
-//   softmax   lazy rescaling: the running max used for exp2 is only moved when
-//             the true max exceeds it by more than 8 (in log2 units), so p <= 256
-//             and the accumulator is rescaled rarely.
-//   order     workgroups of one KV head stay on the same XCDs (they share the
-//             K/V prefix in that XCD's L2); heaviest query tiles first.
+//             staging.  A 3-stage ring keeps two stages (80 KB) in flight while one
+//             is consumed; completion is tracked with explicit vmcnt waits (the
+//             compiler does not track LDS-DMA writes) and one s_barrier per stage.
+//             The kernel must not spill: a scratch reload is a vector-memory op
+//             issued behind the DMA, and waiting for it would drain the ring.
+//             Slots are XOR-swizzled so K operand reads (ds_read_b128) and the
+//             transposing V reads (ds_read_b64_tr_b16) are bank-conflict free.
+//   softmax   lazy rescaling: the running max used for exp2 only moves when the true
+//             max exceeds it by more than 8 (log2 units), so p <= 256 and the
+//             accumulator is rescaled rarely; the scale is folded into one fma.
+//   order     workgroups of one KV head stay on the same XCDs (they share the K/V
+//             prefix in that XCD's L2); heaviest query tiles first.
 namespace pf {
 constexpr int DK = 192, DV = 128, VOFF = 192;
-constexpr int KT = 32;                   // keys per stage
-constexpr int NSTAGE = 6;                // ring: one stage consumed, up to four in flight
-constexpr int NW = 4;
+constexpr int KT = 64;                   // keys per stage
+constexpr int NSTAGE = 3;                // one consumed, two in flight
+constexpr int NW = 8;
+constexpr int ROWS_W = 32;               // rows per wave
 constexpr int KCH = DK * 2 / 16;         // 24 chunks of 16 B per K row
 constexpr int VCH = DV * 2 / 16;         // 16 chunks per V row
-constexpr int KSLOTS = KT * KCH;         // 768
-constexpr int SLOTS = KT * (KCH + VCH);  // 1280
+constexpr int KSLOTS = KT * KCH;         // 1536
+constexpr int SLOTS = KT * (KCH + VCH);  // 2560
 constexpr int PER_WAVE = SLOTS / 64 / NW;  // 5 DMA instructions per wave per stage
-constexpr int STAGE_BYTES = SLOTS * 16;  // 20 KB
+constexpr int STAGE_BYTES = SLOTS * 16;  // 40 KB
 constexpr int BT_MAX = 4096;             // block-table entries staged in LDS
 constexpr int KS = DK / 16;              // 12 k-steps
 constexpr int DB = DV / 32;              // 4 output dim blocks
+static_assert(SLOTS % (64 * NW) == 0, "stage must split evenly over the waves");
 }  // namespace pf
 
 __device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ ((key >> 1) & 7)); }
@@ -313,7 +317,7 @@ __device__ __forceinline__ void pf_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256, 1) void prefill_fast_kernel(PrefillArgs a, int ntile_max) {
+__global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int ntile_max) {
   using namespace pf;
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE_BYTES];
   __shared__ int btl[BT_MAX];
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void prefill_fast_kernel(PrefillArgs a, int
   const int n32 = lane & 31, g = lane >> 5;
   const int Hkv = a.c.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
-  const int TPW = 64 / G;                       // query tokens per wave
+  const int TPW = ROWS_W / G;                   // query tokens per wave
   const int QT = NW * TPW;                      // query tokens per workgroup
   // ---- workgroup -> (sequence, KV head, tile): XCD-aware, heaviest first ----
   const int NH = a.num_seqs * Hkv;
@@ -351,130 +355,119 @@ __global__ __launch_bounds__(256, 1) void prefill_fast_kernel(PrefillArgs a, int
   const int BS = a.c.block_size;
   const int nblk = wg_hi >= 0 ? wg_hi / BS + 1 : 0;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
-  for (int i = threadIdx.x; i < nblk; i += 256) btl[i] = btrow[i];
+  for (int i = threadIdx.x; i < nblk; i += NW * 64) btl[i] = btrow[i];
 
-  // ---- Q rows of this wave into registers (B operand), visibility limits ----
-  bf16x8 qreg[2][KS];
-  int hi[2];
-#pragma unroll
-  for (int rg = 0; rg < 2; ++rg) {
-    const int r = rg * 32 + n32;
-    const int qi = wt0 + r / G, hh = r % G;
-    const bool live = qi < L;
-    hi[rg] = live ? min(off + qi, S - 1) : -1;
-    const uint16_t* qp = a.q + (int64_t)(q0 + (live ? qi : 0)) * a.q_st + (int64_t)(kvh * G + hh) * a.q_sh;
+  // ---- Q rows of this wave into registers (B operand), visibility limit ----
+  bf16x8 qreg[KS];
+  const int qi_lane = wt0 + n32 / G;
+  const bool live = qi_lane < L;
+  const int hi = live ? min(off + qi_lane, S - 1) : -1;
+  {
+    const uint16_t* qp = a.q + (int64_t)(q0 + (live ? qi_lane : 0)) * a.q_st + (int64_t)(kvh * G + n32 % G) * a.q_sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 w = {0, 0, 0, 0};
       if (live) w = *reinterpret_cast<const u32x4*>(qp + ks * 16 + g * 8);
-      qreg[rg][ks] = __builtin_bit_cast(bf16x8, w);
+      qreg[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
   const int wave_last_q = min(wt0 + TPW, L) - 1;
   const int wave_hi = wave_last_q >= wt0 ? min(off + wave_last_q, S - 1) : -1;
   const int wave_lo = off + wt0;                // keys <= wave_lo are visible to every live row
   const float sl2 = a.scale * kLog2e;
+
+  // the (key, byte-in-row) each lane fetches per DMA instruction does not depend on the stage
+  int dkey[PER_WAVE], dbyte[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int slot = (wave * PER_WAVE + u) * 64 + lane;
+    if (slot < KSLOTS) {
+      dkey[u] = slot / KCH;
+      dbyte[u] = ((slot - dkey[u] * KCH) ^ ((dkey[u] >> 1) & 7)) * 16;
+    } else {
+      const int vs = slot - KSLOTS;
+      dkey[u] = vs / VCH;
+      dbyte[u] = VOFF * 2 + ((vs - dkey[u] * VCH) ^ ((dkey[u] & 7) << 1)) * 16;
+    }
+  }
+  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * 2;
   __syncthreads();                              // block table staged; Q loads retired
 
+  // keys past the workgroup's last visible key re-read that key: every block id used
+  // comes from the staged part of the table (entries 0 .. wg_hi / BS)
   auto issue = [&](int st) {
     char* buf = smem + (st % NSTAGE) * STAGE_BYTES;
     const int j0 = st * KT;
-    // keys past the workgroup's last visible key re-read that key: every block id used
-    // comes from the staged part of the table (entries 0 .. wg_hi / BS)
     const int kmax = wg_hi - j0;
-    const int64_t B0 = btl[j0 / BS];
-    const int64_t B1 = btl[min(j0 + 16, wg_hi) / BS];
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      const int i = wave * PER_WAVE + u;
-      const int slot = i * 64 + lane;
-      int key, byte;
-      if (slot < KSLOTS) {
-        key = slot / KCH;
-        byte = ((slot - key * KCH) ^ ((key >> 1) & 7)) * 16;
-      } else {
-        const int vs = slot - KSLOTS;
-        key = vs / VCH;
-        byte = VOFF * 2 + ((vs - key * VCH) ^ ((key & 7) << 1)) * 16;
-      }
-      const int kc = min(key, kmax);
-      const int64_t blk = kc < 16 ? B0 : B1;
-      const int64_t pos = (j0 + kc) % BS;
-      const uint8_t* src = a.c.data + (blk * a.c.sb + pos * a.c.ss + (int64_t)kvh * a.c.sh) * 2 + byte;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, 0);
+      const int j = j0 + min(dkey[u], kmax);
+      const int64_t blk = btl[j / BS];
+      const int64_t pos = j % BS;
+      const uint8_t* src = head_base + (blk * a.c.sb + pos * a.c.ss) * 2 + dbyte[u];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (wave * PER_WAVE + u) * 1024),
+                                       16, 0, 0);
     }
   };
 
-  auto qk = [&](int st, f32x16 (&s)[2]) {
-    const char* buf = smem + (st % NSTAGE) * STAGE_BYTES;
+  f32x16 acc[DB];
+  float m = kNegInf, l = 0.f;
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[rg][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // one 32-key half of a stage: QK^T, online softmax, PV (each half updates (m, l, acc))
+  auto half_step = [&](int j, int h) {
+    const char* buf = smem + (j % NSTAGE) * STAGE_BYTES;
+    const int kb = j * KT + 32 * h;                // first key of the half
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + pf_k_slot(n32, 2 * ks + g) * 16);
-#pragma unroll
-      for (int rg = 0; rg < 2; ++rg) s[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rg][ks], s[rg], 0, 0, 0);
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + pf_k_slot(32 * h + n32, 2 * ks + g) * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
     }
-  };
-
-  f32x16 acc[2][DB];
-  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
-#pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rg][db][i] = 0.f;
-
-  auto softmax_pv = [&](int j, const f32x16 (&s)[2]) {
-    const bool need_mask = j * KT + KT - 1 > wave_lo;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      float x[16];
-      float mx = kNegInf;
+    // online softmax on raw scores; the scale (> 0) is folded into one fma per score
+    float mx = kNegInf;
+    if (kb + 31 > wave_lo) {                       // the causal diagonal crosses this half
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float v = s[rg][i] * sl2;
-        if (need_mask) {
-          const int key = j * KT + 8 * (i >> 2) + 4 * g + (i & 3);
-          v = key <= hi[rg] ? v : kNegInf;
-        }
-        x[i] = v;
-        mx = fmaxf(mx, v);
+        const int key = kb + 8 * (i >> 2) + 4 * g + (i & 3);
+        s[i] = key <= hi ? s[i] : kNegInf;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m[rg], mx);
-      const bool grow = mn > m[rg] + 8.0f;       // true on the first visible key (m = -inf)
-      if (__any(grow)) {
-        const float alpha = grow ? fast_exp2(m[rg] - mn) : 1.0f;
-        m[rg] = grow ? mn : m[rg];
-        l[rg] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha;
-      }
-      const float base = m[rg] == kNegInf ? 0.f : m[rg];
-      float ps = 0.f;
-      uint32_t pk[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(x[2 * i] - base), p1 = fast_exp2(x[2 * i + 1] - base);
-        ps += p0 + p1;
-        pk[i] = pack_bf16x2(p0, p1);
-      }
-      l[rg] += ps;
-      pb[rg][0] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-      pb[rg][1] = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    const float mn = fmaxf(m, mx);
+    const bool grow = mn > m + 8.0f;             // true on the first visible key (m = -inf)
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m - mn) : 1.0f;
+      m = grow ? mn : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    const float nbase = m == kNegInf ? 0.f : -m;
+    uint32_t pk[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], sl2, nbase));
+      const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], sl2, nbase));
+      ps += p0 + p1;
+      pk[i] = pack_bf16x2(p0, p1);
+    }
+    l += ps;
     // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] P^T[16 keys x 32 rows]; the lane's
     // k order (keys 16kh+4g+0..3, then 16kh+8+4g+0..3) matches its own probabilities
-    const char* buf = smem + (j % NSTAGE) * STAGE_BYTES;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int key0 = 16 * kh + 4 * g + (s16 >> 2);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * kh], pk[4 * kh + 1], pk[4 * kh + 2], pk[4 * kh + 3]});
+      const int key0 = 32 * h + 16 * kh + 4 * g + (s16 >> 2);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dim = db * 32 + 16 * half + 4 * (s16 & 3);
@@ -484,65 +477,51 @@ __global__ __launch_bounds__(256, 1) void prefill_fast_kernel(PrefillArgs a, int
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(buf + pf_v_slot(key0 + 8, c) * 16 + inb));
         const bf16x8 vop = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-          acc[rg][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[rg][kh], acc[rg][db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[db], 0, 0, 0);
       }
     }
   };
 
-  // ---- pipeline: stage j is consumed while stages j+1 .. j+NSTAGE-2 are in flight ----
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
-    if (st < nsteps) issue(st);
+  // ---- pipeline: stage j is consumed while stages j+1, j+2 are in flight ----
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
   for (int j = 0; j < nsteps; ++j) {
-    const int ahead = min(NSTAGE - 2, nsteps - 1 - j);   // stages issued after stage j
-    if (ahead >= 4) PF_WAIT_VM(20);
-    else if (ahead == 3) PF_WAIT_VM(15);
-    else if (ahead == 2) PF_WAIT_VM(10);
-    else if (ahead == 1) PF_WAIT_VM(5);
+    if (j + 1 < nsteps) PF_WAIT_VM(5);             // stage j landed; stage j+1 may still fly
     else PF_WAIT_VM(0);
     pf_barrier();                                  // stage j resident for all waves; stage j-1 dead
-    if (j + NSTAGE - 1 < nsteps) issue(j + NSTAGE - 1);
-    if (j * KT <= wave_hi) {
-      f32x16 s[2];
-      qk(j, s);
-      softmax_pv(j, s);
-    }
+    if (j + 2 < nsteps) issue(j + 2);
+    if (j * KT <= wave_hi) half_step(j, 0);
+    if (j * KT + 32 <= wave_hi) half_step(j, 1);
   }
 
-  // ---- normalise and write ----
-#pragma unroll
-  for (int rg = 0; rg < 2; ++rg) {
-    const float lt = l[rg] + __shfl_xor(l[rg], 32, 64);
-    const int r = rg * 32 + n32;
-    const int qi = wt0 + r / G, hh = r % G;
-    if (qi >= L) continue;
+  // ---- normalise and write: lane holds dims db*32 + 8q + 4g + 0..3 of its row ----
+  const float lt = l + __shfl_xor(l, 32, 64);
+  if (live) {
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int64_t tok = q0 + qi, head = kvh * G + hh;
+    const int64_t tok = q0 + qi_lane, head = kvh * G + n32 % G;
     uint16_t* op = a.out + (tok * a.num_q_heads + head) * DV;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        u32x2 pk = {pack_bf16x2(acc[rg][db][4 * qq] * inv, acc[rg][db][4 * qq + 1] * inv),
-                    pack_bf16x2(acc[rg][db][4 * qq + 2] * inv, acc[rg][db][4 * qq + 3] * inv)};
+        u32x2 pk = {pack_bf16x2(acc[db][4 * qq] * inv, acc[db][4 * qq + 1] * inv),
+                    pack_bf16x2(acc[db][4 * qq + 2] * inv, acc[db][4 * qq + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + db * 32 + 8 * qq + 4 * g) = pk;
       }
     if (a.out_lse && g == 0)
-      a.out_lse[tok * a.num_q_heads + head] = lt > 0.f ? (m[rg] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+      a.out_lse[tok * a.num_q_heads + head] = lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
 bool prefill_fast_eligible(const PrefillArgs& a) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   return a.c.esize == 2 && a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192 && a.c.block_size % 16 == 0 &&
-         G >= 1 && 64 % G == 0 && a.bt_stride <= pf::BT_MAX;
+         G >= 1 && pf::ROWS_W % G == 0 && a.bt_stride <= pf::BT_MAX && a.scale > 0.f;
 }
 
 void launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const int QT = pf::NW * (64 / G);
+  const int QT = pf::NW * (pf::ROWS_W / G);
   const int ntile_max = (a.max_q + QT - 1) / QT;
   const int NH = a.num_seqs * a.c.num_kv_heads;
   int grid;
@@ -553,7 +532,7 @@ void launch_prefill_fast(const PrefillArgs& a, hipStream_t s) {
     grid = ntile_max * NH;
   }
   if (grid == 0) return;
-  hipLaunchKernelGGL(prefill_fast_kernel, dim3(grid), dim3(256), 0, s, a, ntile_max);
+  hipLaunchKernelGGL(prefill_fast_kernel, dim3(grid), dim3(pf::NW * 64), 0, s, a, ntile_max);
 }
 
 }  // namespace pa
