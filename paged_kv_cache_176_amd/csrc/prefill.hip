@@ -267,7 +267,7 @@ bool launch_prefill(const PrefillArgs& a, hipStream_t s) {
 }
 
 // ===========================================================================
-// Fast path: bf16 DiffKV rows (K 192 / V 128), block size a multiple of 16.
+// Fast path: bf16 DiffKV rows (K 192 / V 128), block size a power of two >= 16.
 //
 //   rows      workgroup = 8 waves x 32 rows (32 query tokens x 8 GQA heads for G = 8);
 //             a wave's 32 rows are one v_mfma_f32_32x32x16_bf16 column block, whose
@@ -352,8 +352,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
   const int wg_last_q = min(tile * QT + QT, L) - 1;
   const int wg_hi = min(off + wg_last_q, S - 1);
   const int nsteps = wg_hi >= 0 ? wg_hi / KT + 1 : 0;
-  const int BS = a.c.block_size;
-  const int nblk = wg_hi >= 0 ? wg_hi / BS + 1 : 0;
+  const int bs_shift = __builtin_ctz(a.c.block_size);   // block size is a power of two here
+  const int bs_mask = a.c.block_size - 1;
+  const int nblk = wg_hi >= 0 ? (wg_hi >> bs_shift) + 1 : 0;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
   for (int i = threadIdx.x; i < nblk; i += NW * 64) btl[i] = btrow[i];
 
@@ -391,6 +392,21 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     }
   }
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * 2;
+  // lane byte offsets of the K operand reads (per r = ks % 4) and of the transposed V
+  // reads (per 32-dim block), relative to the stage buffer
+  int koff[4], voff[DB];
+  {
+    const int sw = (n32 >> 1) & 7;                // = ((32h + n32) >> 1) & 7 for both halves
+#pragma unroll
+    for (int r = 0; r < 4; ++r) koff[r] = (n32 * KCH + ((2 * r + g) ^ sw)) * 16;
+    const int s16 = lane & 15, half = (lane >> 4) & 1;
+    const int vkey = 4 * g + (s16 >> 2);          // key within a 16-key chunk (the +8 row keeps key & 7)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dim = db * 32 + 16 * half + 4 * (s16 & 3);
+      voff[db] = pf_v_slot(vkey, dim >> 3) * 16 + (dim & 7) * 2;
+    }
+  }
   __syncthreads();                              // block table staged; Q loads retired
 
   // keys past the workgroup's last visible key re-read that key: every block id used
@@ -402,8 +418,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const int j = j0 + min(dkey[u], kmax);
-      const int64_t blk = btl[j / BS];
-      const int64_t pos = j % BS;
+      const int64_t blk = btl[j >> bs_shift];
+      const int64_t pos = j & bs_mask;
       const uint8_t* src = head_base + (blk * a.c.sb + pos * a.c.ss) * 2 + dbyte[u];
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (wave * PER_WAVE + u) * 1024),
                                        16, 0, 0);
@@ -424,9 +440,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    // chunk 2ks+g of key 32h+n32: ks = 4t+r -> slot = key*24 + 8t + ((2r+g) ^ swizzle), so
+    // the lane-dependent part is koff[r] and t, h enter as immediate offsets
+    const char* kbuf = buf + h * (32 * KCH * 16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + pf_k_slot(32 * h + n32, 2 * ks + g) * 16);
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks & 3] + (ks >> 2) * 128);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
     }
     // online softmax on raw scores; the scale (> 0) is folded into one fma per score
@@ -463,19 +482,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     l += ps;
     // O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] P^T[16 keys x 32 rows]; the lane's
     // k order (keys 16kh+4g+0..3, then 16kh+8+4g+0..3) matches its own probabilities
-    const int s16 = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * kh], pk[4 * kh + 1], pk[4 * kh + 2], pk[4 * kh + 3]});
-      const int key0 = 32 * h + 16 * kh + 4 * g + (s16 >> 2);
+      // source row key = 32h + 16kh + (4g + s16/4) [+ 8]: the swizzle depends only on the lane
+      // part, so h, kh and the +8 row are immediate offsets on voff[db]
+      const char* vbuf = buf + (32 * h + 16 * kh) * (VCH * 16);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int dim = db * 32 + 16 * half + 4 * (s16 & 3);
-        const int c = dim >> 3, inb = (dim & 7) * 2;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(buf + pf_v_slot(key0, c) * 16 + inb));
+            (__attribute__((address_space(3))) s16x4*)(vbuf + voff[db]));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(buf + pf_v_slot(key0 + 8, c) * 16 + inb));
+            (__attribute__((address_space(3))) s16x4*)(vbuf + voff[db] + 8 * VCH * 16));
         const bf16x8 vop = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[db], 0, 0, 0);
       }
@@ -515,7 +533,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
 
 bool prefill_fast_eligible(const PrefillArgs& a) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  return a.c.esize == 2 && a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192 && a.c.block_size % 16 == 0 &&
+  const int bs = a.c.block_size;
+  return a.c.esize == 2 && a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192 && bs >= 16 && (bs & (bs - 1)) == 0 &&
          G >= 1 && pf::ROWS_W % G == 0 && a.bt_stride <= pf::BT_MAX && a.scale > 0.f;
 }
 
