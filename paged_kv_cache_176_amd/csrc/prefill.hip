@@ -307,7 +307,11 @@ constexpr int DB = DV / 32;              // 4 output dim blocks
 static_assert(SLOTS % (64 * NW) == 0, "stage must split evenly over the waves");
 }  // namespace pf
 
-__device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ ((key >> 1) & 7)); }
+// K chunk swizzle: a permutation over any 8 consecutive keys and distinct in (key parity,
+// swizzle) over 16 keys, so 16-byte operand reads are conflict-free whether the LDS serves
+// 8 lanes over 32 banks or 16 lanes over 64 banks per cycle.  Depends on key bits 0-3 only.
+__device__ __forceinline__ int pf_k_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
+__device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ pf_k_swz(key)); }
 __device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ ((key & 7) << 1)); }
 
 #define PF_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     const int slot = (wave * PER_WAVE + u) * 64 + lane;
     if (slot < KSLOTS) {
       dkey[u] = slot / KCH;
-      dbyte[u] = ((slot - dkey[u] * KCH) ^ ((dkey[u] >> 1) & 7)) * 16;
+      dbyte[u] = ((slot - dkey[u] * KCH) ^ pf_k_swz(dkey[u])) * 16;
     } else {
       const int vs = slot - KSLOTS;
       dkey[u] = vs / VCH;
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
   // reads (per 32-dim block), relative to the stage buffer
   int koff[4], voff[DB];
   {
-    const int sw = (n32 >> 1) & 7;                // = ((32h + n32) >> 1) & 7 for both halves
+    const int sw = pf_k_swz(n32);                 // = pf_k_swz(32h + n32) for both halves
 #pragma unroll
     for (int r = 0; r < 4; ++r) koff[r] = (n32 * KCH + ((2 * r + g) ^ sw)) * 16;
     const int s16 = lane & 15, half = (lane >> 4) & 1;
@@ -500,6 +504,93 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     }
   };
 
+  // A whole stage with no causal mask (every key visible to every live row of the wave),
+  // software-pipelined inside the wave:  QK0 | QK1 + softmax0 | PV0 + softmax1 | PV1.
+  // The scheduler is asked to interleave one MFMA with a few VALU/transcendental ops in
+  // the two overlapped regions; the rare accumulator rescale sits between regions.
+  auto qk_half = [&](const char* buf, int h, f32x16& s) {
+    const char* kbuf = buf + h * (32 * KCH * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks & 3] + (ks >> 2) * 128);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
+    }
+  };
+  // softmax of one unmasked half: updates m and l, returns P as bf16 and the factor the
+  // accumulator must be scaled by before this half's PV (1 unless the max grew)
+  auto softmax_half = [&](f32x16& s, uint32_t (&pk)[8]) -> float {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    const float mn = fmaxf(m, mx);
+    const bool grow = mn > m + 8.0f;
+    const float alpha = grow ? fast_exp2(m - mn) : 1.0f;
+    m = grow ? mn : m;
+    const float nbase = -m;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], sl2, nbase));
+      const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], sl2, nbase));
+      ps += p0 + p1;
+      pk[i] = pack_bf16x2(p0, p1);
+    }
+    l = l * alpha + ps;
+    return alpha;
+  };
+  auto pv_half = [&](const char* buf, int h, const uint32_t (&pk)[8]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * kh], pk[4 * kh + 1], pk[4 * kh + 2], pk[4 * kh + 3]});
+      const char* vbuf = buf + (32 * h + 16 * kh) * (VCH * 16);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vbuf + voff[db]));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vbuf + voff[db] + 8 * VCH * 16));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto bulk_stage = [&](int j) {
+    const char* buf = smem + (j % NSTAGE) * STAGE_BYTES;
+    f32x16 s0, s1;
+    uint32_t p0[8], p1[8];
+    qk_half(buf, 0, s0);
+    // region 1: QK of the second half while the first half's softmax runs
+    qk_half(buf, 1, s1);
+    const float a0 = softmax_half(s0, p0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // ds_read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // mfma
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 1);   // valu / trans
+    }
+    if (__any(a0 != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= a0;
+    }
+    // region 2: PV of the first half while the second half's softmax runs
+    pv_half(buf, 0, p0);
+    const float a1 = softmax_half(s1, p1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);   // ds_read (two transposed reads)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // mfma
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 2);   // valu / trans
+    }
+    if (__any(a1 != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= a1;
+    }
+    pv_half(buf, 1, p1);
+  };
+
   // ---- pipeline: stage j is consumed while stages j+1, j+2 are in flight ----
   if (nsteps > 0) issue(0);
   if (nsteps > 1) issue(1);
@@ -508,8 +599,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     else PF_WAIT_VM(0);
     pf_barrier();                                  // stage j resident for all waves; stage j-1 dead
     if (j + 2 < nsteps) issue(j + 2);
-    if (j * KT <= wave_hi) half_step(j, 0);
-    if (j * KT + 32 <= wave_hi) half_step(j, 1);
+    if (wave_hi >= 0 && j * KT + KT - 1 <= wave_lo) {
+      bulk_stage(j);                               // no key of the stage is masked for this wave
+    } else {
+      if (j * KT <= wave_hi) half_step(j, 0);
+      if (j * KT + 32 <= wave_hi) half_step(j, 1);
+    }
   }
 
   // ---- normalise and write: lane holds dims db*32 + 8q + 4g + 0..3 of its row ----
