@@ -306,7 +306,7 @@ def main():
                                                         kv_gbs=round(c2.kv_bytes / k2 / 1e9, 1),
                                                         step_gbs=round((c2.kv_bytes + c2.other_bytes) / d2 / 1e9, 1))
             del c2
-        for b2, p2 in [(1, 256), (16, 32)]:
+        for b2, p2 in [(1, 256), (16, 16)]:
             w2 = workloads.mla_decode(b2, 100000)
             c2 = DecodeCase(w2, p2)
             d2, k2 = time_steps(c2.step, 50, 5, events=True)
