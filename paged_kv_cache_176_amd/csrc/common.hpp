@@ -55,4 +55,11 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Read-only int at a wave-uniform address, through the scalar data cache
+// (s_load_dword).  Waited on by lgkmcnt, so it never has to drain the vector
+// memory counter that tracks the K/V prefetch.  Every lane must pass the same p.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 }  // namespace pa

@@ -43,9 +43,12 @@ struct TileRegs {
   u32x4 v[kV];
 };
 
-template <int DK, int DV, int VOFF, int NR, bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
+// BLK16: block_size is a multiple of 16, so a 16-key tile (tiles start at multiples
+// of 16) sits in one block and its table entry is wave-uniform.
+template <int DK, int DV, int VOFF, int NR, bool FP8, int NW, bool BLK16>
+__global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_partial_kernel(SplitArgs a) {
   using Regs = TileRegs<DK, DV, VOFF, FP8>;
+  constexpr int NBUF = (FP8 && NR == 1) ? 3 : 2;  // fp8 tiles are half the bytes: two in flight where registers allow
   constexpr int KS = DK / 32;        // MFMA k-steps of QK^T
   constexpr int DB = DV / 16;        // 16-dim blocks of PV
   constexpr int VP = DV + 16;        // LDS row pitch of the V tile (elements), 32 B pad
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
@@ -97,6 +100,10 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
     vscale = a.c.scale_mode == 2 ? a.c.v_scale[kvh] : a.c.v_scale[0];
   }
   const float sl2 = a.scale * kLog2e * kscale;
+  // Q is complete in registers from here on.  Without this wait the compiler, which
+  // counts vector loads in issue order, would wait at Q's first use in the loop for
+  // every K/V load issued after it, emptying the prefetch on each tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   f32x4 acc[NR][DB];
   float m[NR], l[NR];
@@ -113,10 +120,21 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
   const int esz = FP8 ? 1 : 2;
 
+  // With BLK16 the tile's block id comes in by a scalar load, which leaves the
+  // vector memory counter to the K/V prefetch alone; otherwise each lane looks up
+  // its own key's block (and that load's wait also drains the prefetch).
   auto load_tile = [&](Regs& R, int ti) {
-    const int j = min(start + ti * 16 + n, S - 1);          // clamp: never past the sequence
-    const int64_t blk = btrow[j / a.c.block_size];
-    const int64_t pos = j % a.c.block_size;
+    int64_t blk;
+    int pos;
+    if constexpr (BLK16) {
+      const int j0 = __builtin_amdgcn_readfirstlane(start + ti * 16);
+      blk = load_uniform(btrow + j0 / a.c.block_size);
+      pos = j0 % a.c.block_size + min(n, S - 1 - j0);      // clamp: never past the sequence
+    } else {
+      const int j = min(start + ti * 16 + n, S - 1);
+      blk = btrow[j / a.c.block_size];
+      pos = j % a.c.block_size;
+    }
     const uint8_t* row = cbase + (blk * a.c.sb + pos * a.c.ss + (int64_t)kvh * a.c.sh) * esz;
 #pragma unroll
     for (int i = 0; i < Regs::kK; ++i)
@@ -126,6 +144,9 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
       for (int i = 0; i < Regs::kV; ++i)
         R.v[i] = *reinterpret_cast<const u32x4*>(row + (FP8 ? VOFF + i * 64 + g * 16 : (VOFF + i * 32 + g * 8) * 2));
     }
+    // keep the scheduler from sinking these loads below the next tile's compute
+    // (it would then wait for that tile before issuing them: one tile in flight)
+    if constexpr (NR != 4) __builtin_amdgcn_sched_barrier(0);
   };
 
   auto compute_tile = [&](const Regs& R, int ti) {
@@ -213,8 +234,15 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
     }
   };
 
-  // ---- main loop: this wave's tiles wave, wave+NW, ... with 2 register buffers ----
-  {
+  // ---- main loop: this wave's tiles wave, wave+NW, ... through a ring of NBUF
+  // register buffers, NBUF - 1 tiles in flight while one is computed.  Loads are
+  // issued unconditionally (indices past the end re-read the partition's last tile,
+  // which is in cache) so that every compute waits for exactly its own buffer: a
+  // skipped load on some path would make the compiler's in-order load counting
+  // wait for the whole ring.
+  if constexpr (NR == 4) {
+    // 64 rows fill the register file: the unconditional form spills here, so the
+    // loads past the end are skipped instead
     Regs b0, b1;
     int ti = wave;
     if (ti < nt) load_tile(b0, ti);
@@ -227,6 +255,39 @@ __global__ __launch_bounds__(NW * 64) void splitkv_partial_kernel(SplitArgs a) {
       if (t2 < nt) load_tile(b0, t2);
       compute_tile(b1, t1);
       ti = t2;
+    }
+  } else if (wave < nt) {
+    // one exit per loop (a break in mid-body gives the structurizer an extra edge
+    // into the loop header that carries the previous half's loads as pending)
+    auto ahead = [&](int t) { return min(t, nt - 1); };
+    int ti = wave;
+    if constexpr (NBUF == 2) {
+      Regs b0, b1;
+      load_tile(b0, ti);
+      while (ti + NW < nt) {
+        load_tile(b1, ti + NW);
+        compute_tile(b0, ti);
+        load_tile(b0, ahead(ti + 2 * NW));
+        compute_tile(b1, ti + NW);
+        ti += 2 * NW;
+      }
+      if (ti < nt) compute_tile(b0, ti);
+    } else {
+      static_assert(NBUF == 3, "register ring of 2 or 3 tiles");
+      Regs b0, b1, b2;
+      load_tile(b0, ti);
+      load_tile(b1, ahead(ti + NW));
+      while (ti + 2 * NW < nt) {
+        load_tile(b2, ti + 2 * NW);
+        compute_tile(b0, ti);
+        load_tile(b0, ahead(ti + 3 * NW));
+        compute_tile(b1, ti + NW);
+        load_tile(b1, ahead(ti + 4 * NW));
+        compute_tile(b2, ti + 2 * NW);
+        ti += 3 * NW;
+      }
+      if (ti < nt) compute_tile(b0, ti);
+      if (ti + NW < nt) compute_tile(b1, ti + NW);
     }
   }
 
@@ -369,7 +430,10 @@ struct SplitKernel {
   static constexpr int kLds = kLdsV > kLdsM ? kLdsV : kLdsM;
   static void launch(const SplitArgs& a, hipStream_t s) {
     dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(NW * 64);
-    hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW>), grid, block, 0, s, a);
+    if ((a.c.block_size & 15) == 0)
+      hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((splitkv_partial_kernel<DK, DV, VOFF, NR, FP8, NW, false>), grid, block, 0, s, a);
   }
 };
 
