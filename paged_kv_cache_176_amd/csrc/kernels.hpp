@@ -43,9 +43,6 @@ struct SplitArgs {
 
 bool splitkv_supported(const SplitArgs& a);
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s);
-// LDS-streamed variant for wide bf16 rows (splitkv_lds.hip)
-bool splitkv_lds_eligible(const SplitArgs& a);
-void launch_splitkv_lds(const SplitArgs& a, hipStream_t s);
 
 struct MergeArgs {
   const float* part_out; const float* part_lse;

@@ -476,10 +476,6 @@ bool splitkv_supported(const SplitArgs& a) {
 }
 
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
-  if (splitkv_lds_eligible(a)) {
-    launch_splitkv_lds(a, s);
-    return true;
-  }
   return dispatch(a, [&](auto k) { decltype(k)::launch(a, s); });
 }
 
