@@ -55,6 +55,21 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4 with the
+// nontemporal hint): lane i's bytes land at lds_base + 16*i, lds_base wave-uniform.
+// Inline asm on purpose: the compiler's wait-count pass does not know which LDS reads
+// these writes feed and answers with vmcnt(0) before some of them, which would empty
+// a load ring on every tile.  Callers wait with explicit vmcnt counts instead.
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // Read-only int at a wave-uniform address, through the scalar data cache
 // (s_load_dword).  Waited on by lgkmcnt, so it never has to drain the vector
 // memory counter that tracks the K/V prefetch.  Every lane must pass the same p.
