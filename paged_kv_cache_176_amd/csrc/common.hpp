@@ -22,16 +22,35 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max / sum over the four 16-lane groups that hold the same MFMA output column.
+// Max / sum over the four 16-lane groups (rows) that hold the same MFMA output
+// column.  v_permlane32_swap / v_permlane16_swap exchange rows in the VALU (no LDS
+// round trip): with both operands v, each lane ends up with the pair {its value, the
+// value 32 (then 16) lanes away}, in the same order on both lanes of the pair.  Inline
+// asm: given two equal operands the compiler assumes the swap returns them unchanged
+// and drops one of the pair.
+__device__ __forceinline__ void swap_rows32(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap_rows16(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
 __device__ __forceinline__ float max_over_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  float x = v, y = v;
+  swap_rows32(x, y);
+  v = fmaxf(x, y);
+  x = v;
+  y = v;
+  swap_rows16(x, y);
+  return fmaxf(x, y);
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  float x = v, y = v;
+  swap_rows32(x, y);
+  v = x + y;
+  x = v;
+  y = v;
+  swap_rows16(x, y);
+  return x + y;
 }
 
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
@@ -64,6 +83,28 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+// Same copy without the nontemporal hint (lines stay in L2 for a neighbour that
+// reads the other part of them).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+// Scalar-base forms: address = sbase (wave-uniform, SGPRs) + voff (per lane, 32-bit),
+// which spares the 64-bit per-lane address arithmetic.
+__device__ __forceinline__ void dma16_nt_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

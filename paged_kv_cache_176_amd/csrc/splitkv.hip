@@ -364,8 +364,8 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
 // ---------------------------------------------------------------------------
 // Merge (attn_merge_lse, and the second kernel of attn_decode_splitkv / attn_verify).
 // Grid: (row * Hq + head, slice of 4*SLOTS output dims).  The workgroup's threads
-// are SLOTS float4 columns x NG partition groups, so each thread issues all of
-// its P / NG partial loads at once; group sums are combined in LDS in a fixed
+// are SLOTS float4 columns x NG partition groups; each thread's partial loads are
+// issued before the log-sum-exp pass; group sums are combined in LDS in a fixed
 // order.  w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p, lse = M + ln sum w_p;
 // M = -inf (no partition saw a key) gives out = 0, lse = -inf, never NaN.
 template <int NT, int SLOTS>
@@ -376,6 +376,19 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __shared__ f32x4 gs[NG][SLOTS];
   const int64_t rh = blockIdx.x;                     // row * Hq + head
   const int P = a.num_partitions, DV = a.dv;
+  const int slot = threadIdx.x % SLOTS, grp = threadIdx.x / SLOTS;
+  const int c4 = blockIdx.y * SLOTS + slot;          // float4 column
+  const bool col_ok = c4 * 4 < DV;
+  const float* po = a.part_out + rh * P * DV + c4 * 4;
+  // this thread's first PRE partials are loaded before the log-sum-exp pass, so that
+  // for P <= PRE * NG the whole merge waits on memory once
+  constexpr int PRE = 4;
+  f32x4 pre[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int p = grp + k * NG;
+    pre[k] = (col_ok && p < P) ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float* lse = a.part_lse + rh * P;
   float mx = kNegInf;
   for (int p = threadIdx.x; p < P; p += NT) mx = fmaxf(mx, lse[p]);
@@ -397,21 +410,14 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   float tot = 0.f;
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const bool empty = (M == kNegInf || tot == 0.f);
-  const int slot = threadIdx.x % SLOTS, grp = threadIdx.x / SLOTS;
-  const int c4 = blockIdx.y * SLOTS + slot;          // float4 column
-  const float* po = a.part_out + rh * P * DV + c4 * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (c4 * 4 < DV) {
-    int p = grp;
-    for (; p + 3 * NG < P; p += 4 * NG) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + NG) * DV);
-      const f32x4 v2 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + 2 * NG) * DV);
-      const f32x4 v3 = *reinterpret_cast<const f32x4*>(po + (int64_t)(p + 3 * NG) * DV);
-      acc += v0 * wsh[p] + v1 * wsh[p + NG] + v2 * wsh[p + 2 * NG] + v3 * wsh[p + 3 * NG];
-    }
-    for (; p < P; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int p = grp + k * NG;
+    if (p < P) acc += pre[k] * wsh[p];
   }
+  if (col_ok)
+    for (int p = grp + PRE * NG; p < P; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
   gs[grp][slot] = acc;
   __syncthreads();
   if (threadIdx.x < SLOTS && c4 * 4 < DV) {

@@ -32,9 +32,14 @@ constexpr int NW = 4;
 constexpr int TT = 16;                 // keys per tile
 }  // namespace sd
 
-// chunk swizzle, as in the prefill kernel: conflict-free 16-byte reads for 8- and
-// 16-lane LDS passes; depends on key bits 0-3 only
+// chunk swizzles (XOR on a row's 16-byte chunk index) that keep 16 lanes reading
+// 16 different rows conflict-free.  640- and 1152-byte rows (bf16): as in the prefill
+// kernel, within groups of 8 chunks.  320-byte rows (fp8): a row pitch of 20 chunks
+// leaves only 4 distinct bank offsets per 4 rows, so chunks are permuted within
+// groups of 4 by ((key >> 2) ^ (key >> 1)) & 3, distinct for the 4 keys of one
+// offset class and for the 4 keys of one parity in every 8-key half.
 __device__ __forceinline__ int sd_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
+__device__ __forceinline__ int sd_swz4(int key) { return ((key >> 2) ^ (key >> 1)) & 3; }
 
 // wait until at most N vector-memory ops of this wave are in flight
 template <int N>
@@ -43,21 +48,28 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DK, int DV, int VOFF, int NR, int NST, int MINW>
+// FP8: E4M3FN rows; K chunks are converted to bf16 at the MFMA, V chunks are converted
+// into a per-wave bf16 [key][dim] tile for the transposing read.  NTL: nontemporal DMA.
+template <int DK, int DV, int VOFF, int NR, int NST, int MINW, bool FP8, bool NTL>
 __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArgs a) {
   using namespace sd;
-  constexpr int ROWB = (VOFF >= DK ? DK + DV : DK) * 2;   // bytes of a row that are read
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int ROWB = (VOFF >= DK ? DK + DV : DK) * ESZ; // bytes of a row that are read
   constexpr int CH = ROWB / 16;                           // 16-byte chunks per row
   constexpr int NINS = TT * CH / 64;                      // DMA instructions per tile
   constexpr int TILE_BYTES = TT * CH * 16;
   constexpr int KS = DK / 32;
   constexpr int DB = DV / 16;
   constexpr int ROWS = NR * 16;
+  constexpr int VP = DV + 16;                             // fp8: bf16 V tile pitch (elements)
+  constexpr int WAVE_BYTES = NST * TILE_BYTES;
+  static_assert(!FP8 || TT * VP * 2 <= TILE_BYTES, "fp8: the bf16 V tile reuses its stage");
   constexpr int MERGE_PITCH = DV + 4;
-  constexpr int RING = NW * NST * TILE_BYTES;
+  constexpr int RING = NW * WAVE_BYTES;
   constexpr int MERGE = NW * ROWS * 2 * 4 + ROWS * MERGE_PITCH * 4;
   constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
-  static_assert(CH % 8 == 0 && (TT * CH) % 64 == 0, "row must be whole 128-byte groups");
+  static_assert(CH % (FP8 ? 4 : 8) == 0 && (TT * CH) % 64 == 0, "row must be whole swizzle groups");
+  static_assert(!FP8 || (VOFF == DK && DK % 64 == 0 && DV % 64 == 0), "fp8: V follows K, 64-byte pieces");
   static_assert(VOFF % 8 == 0 && (VOFF >= DK || VOFF + DV <= DK), "V must be whole chunks of the row");
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
@@ -89,21 +101,51 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     const uint16_t* qp = a.q + (int64_t)(q0 + (live ? qi : 0)) * a.q_st + (int64_t)(kvh * G + hh) * a.q_sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // fp8 pairs k-steps so that one 16-byte chunk of 16 fp8 values feeds two of them
+      const int d0 = FP8 ? (ks >> 1) * 64 + g * 16 + (ks & 1) * 8 : ks * 32 + g * 8;
       u32x4 w = {0, 0, 0, 0};
-      if (live) w = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
+      if (live) w = *reinterpret_cast<const u32x4*>(qp + d0);
       qreg[rg][ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  const float sl2 = a.scale * kLog2e;
+  float kscale = 1.0f, vscale = 1.0f;
+  if (FP8 && a.c.scale_mode != 0) {
+    kscale = a.c.scale_mode == 2 ? a.c.k_scale[kvh] : a.c.k_scale[0];
+    vscale = a.c.scale_mode == 2 ? a.c.v_scale[kvh] : a.c.v_scale[0];
+  }
+  float sl2 = a.scale * kLog2e * kscale;
+  if (sl2 < 0.f) {                               // s * sl2 == (-s) * (-sl2): negate Q (exact)
+#pragma unroll
+    for (int rg = 0; rg < NR; ++rg)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qreg[rg][ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qreg[rg][ks]) ^ 0x80008000u);
+    sl2 = -sl2;
+  }
+  // last key that every live row of this workgroup sees (tiles ending at or before it
+  // need no mask); rows past the query tokens never see any key and are ignored
+  int vis_hi = 0x7fffffff;
+#pragma unroll
+  for (int rg = 0; rg < NR; ++rg) {
+    const int qi = (rg * 16 + n) / G;
+    if (qi < L && qi < a.max_q) vis_hi = min(vis_hi, hi[rg]);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) vis_hi = min(vis_hi, __shfl_xor(vis_hi, o, 64));
+  vis_hi = __builtin_amdgcn_readfirstlane(vis_hi);
 
   // lane byte offsets inside a tile: K operand chunk 4ks+g of key n (per ks parity; the
   // rest of ks is an immediate) and the transposed V source (per 16-dim block, mod 4)
-  const int sw = sd_swz(n);
+  const int sw = FP8 ? sd_swz4(n) : sd_swz(n);
   int koff[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) koff[par] = (n * CH + ((4 * par + g) ^ sw)) * 16;
   int voff[4];
-  {
+  if constexpr (FP8) {
+    // transposing reads from the bf16 V tile: key 4g + n/4, dims 16*db + 4*(n%4)
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) voff[d4] = ((4 * g + (n >> 2)) * VP + 16 * d4 + 4 * (n & 3)) * 2;
+  } else {
     const int vkey = 4 * g + (n >> 2);
     const int vsw = sd_swz(vkey);
 #pragma unroll
@@ -122,11 +164,25 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  char* ring = smem + wave * NST * TILE_BYTES;
-  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * 2;
+  char* ring = smem + wave * WAVE_BYTES;
+  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
   // Q is complete in registers before the first DMA: the explicit vmcnt waits below
   // count DMA instructions only
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
+
+  // lane's source offset (bytes from the tile's first row) for DMA instruction u:
+  // 16-byte slot u*64 + lane of the tile holds chunk c of key `key`, swizzled
+  const int ssb = (int)(a.c.ss * ESZ);           // bytes between consecutive slots
+  auto dma_off = [&](int u, int kmax) {
+    const int slot = u * 64 + lane;
+    const int key = slot / CH;
+    const int c = (slot - key * CH) ^ (FP8 ? sd_swz4(key) : sd_swz(key));
+    return min(key, kmax) * ssb + c * 16;
+  };
+  constexpr bool kKeepOff = NINS <= 10;          // precomputed offsets (MLA rows: registers are full)
+  int off[kKeepOff ? NINS : 1];
+#pragma unroll
+  for (int u = 0; u < (kKeepOff ? NINS : 0); ++u) off[u] = dma_off(u, TT - 1);
 
   auto issue = [&](int ti, int stage) {
     char* buf = ring + stage * TILE_BYTES;
@@ -134,64 +190,111 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     // wave-uniform and comes in by a scalar load (lgkmcnt, not the DMA's vmcnt)
     const int t0 = __builtin_amdgcn_readfirstlane(start + ti * TT);
     const int64_t blk = load_uniform(btrow + (t0 >> bs_shift));
-    const uint8_t* tile = head_base + (blk * a.c.sb + (int64_t)(t0 & bs_mask) * a.c.ss) * 2;
+    const uint8_t* tile = head_base + (blk * a.c.sb + (int64_t)(t0 & bs_mask) * a.c.ss) * ESZ;
     const int kmax = end - 1 - t0;                // keys past the partition re-read its last key
+    const bool full = kmax >= TT - 1;
 #pragma unroll
     for (int u = 0; u < NINS; ++u) {
-      const int slot = u * 64 + lane;
-      const int key = slot / CH;
-      const int c = (slot - key * CH) ^ sd_swz(key);
-      const uint8_t* src = tile + (int64_t)min(key, kmax) * a.c.ss * 2 + c * 16;
-      dma16_nt(src, lds_addr(buf + u * 1024));
+      const uint32_t o = (kKeepOff && full) ? off[u] : dma_off(u, kmax);
+      if constexpr (NTL) dma16_nt_s(o, tile, lds_addr(buf + u * 1024));
+      else dma16_s(o, tile, lds_addr(buf + u * 1024));
     }
   };
 
   auto compute = [&](int ti, int stage) {
-    const char* buf = ring + stage * TILE_BYTES;
+    char* buf = ring + stage * TILE_BYTES;
     const int j0 = start + ti * TT;
     f32x4 s[NR];
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) s[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+      // the tile's fp8 K and V chunks into registers; the stage is then free for the
+      // bf16 [key][dim] V tile that the transposing reads need
+      u32x4 kw[KS / 2], vw[DV / 64];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + koff[ks & 1] + (ks >> 1) * 128);
+      for (int j = 0; j < KS / 2; ++j) kw[j] = *reinterpret_cast<const u32x4*>(buf + koff[0] + j * 64);
 #pragma unroll
-      for (int rg = 0; rg < NR; ++rg) s[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[rg][ks], s[rg], 0, 0, 0);
+      for (int i = 0; i < DV / 64; ++i) vw[i] = *reinterpret_cast<const u32x4*>(buf + koff[0] + (VOFF / 16 + 4 * i) * 16);
+#pragma unroll
+      for (int i = 0; i < DV / 64; ++i) {
+        const u32x2 t0 = fp8x4_to_bf16x4(vw[i][0]), t1 = fp8x4_to_bf16x4(vw[i][1]);
+        const u32x2 t2 = fp8x4_to_bf16x4(vw[i][2]), t3 = fp8x4_to_bf16x4(vw[i][3]);
+        char* dst = buf + (n * VP + i * 64 + g * 16) * 2;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{t0[0], t0[1], t1[0], t1[1]};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{t2[0], t2[1], t3[0], t3[1]};
+      }
+      // K: one 16-byte chunk (dims 64j + 16g .. +16) feeds k-steps 2j and 2j + 1
+#pragma unroll
+      for (int j = 0; j < KS / 2; ++j) {
+        const u32x4 w = kw[j];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2 c0 = fp8x4_to_bf16x4(w[2 * h]), c1 = fp8x4_to_bf16x4(w[2 * h + 1]);
+          const bf16x8 kop = __builtin_bit_cast(bf16x8, u32x4{c0[0], c0[1], c1[0], c1[1]});
+#pragma unroll
+          for (int rg = 0; rg < NR; ++rg)
+            s[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[rg][2 * j + h], s[rg], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(buf + koff[ks & 1] + (ks >> 1) * 128);
+#pragma unroll
+        for (int rg = 0; rg < NR; ++rg)
+          s[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[rg][ks], s[rg], 0, 0, 0);
+      }
     }
     s16x4 pb[NR];
+    // every live row sees every key of the tile: no mask, and the scale (>= 0 here)
+    // folds into the max and into one fma per score
+    const bool nomask = j0 + TT - 1 <= vis_hi;
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
       float x[4];
       float mx = kNegInf;
+      if (nomask) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 4 * g + i;
-        x[i] = (j <= hi[rg]) ? s[rg][i] * sl2 : kNegInf;
-        mx = fmaxf(mx, x[i]);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rg][i]);
+        mx = max_over_groups(mx) * sl2;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * g + i;
+          x[i] = (j <= hi[rg]) ? s[rg][i] * sl2 : kNegInf;
+          mx = fmaxf(mx, x[i]);
+        }
+        mx = max_over_groups(mx);
       }
-      mx = max_over_groups(mx);
+      // lazy rescaling: the running max used as the exp2 base moves only when the
+      // tile's max exceeds it by more than 8 (log2 units), so p <= 256 and the
+      // accumulator is rescaled on few tiles; (m, l, acc) stay consistent throughout
       const float mn = fmaxf(m[rg], mx);
-      const float base = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(m[rg] - base);
-      float p[4], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(x[i] - base);
-        ps += p[i];
-      }
-      l[rg] = l[rg] * alpha + ps;
-      m[rg] = mn;
-      if (__any(alpha != 1.0f)) {
+      const bool grow = mn > m[rg] + 8.0f;        // true on the first visible key (m = -inf)
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2(m[rg] - mn) : 1.0f;
+        m[rg] = grow ? mn : m[rg];
+        l[rg] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[rg][db] *= alpha;
       }
+      const float base = (m[rg] == kNegInf) ? 0.f : m[rg];
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(nomask ? __builtin_fmaf(s[rg][i], sl2, -base) : x[i] - base);
+        ps += p[i];
+      }
+      l[rg] += ps;
       u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       pb[rg] = __builtin_bit_cast(s16x4, pk);
     }
+    __builtin_amdgcn_wave_barrier();
+    const char* vsrc = buf;                       // fp8: the bf16 V tile written above
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(buf + voff[db & 3] + (db >> 2) * 128));
+          (__attribute__((address_space(3))) s16x4*)(vsrc + voff[db & 3] + (db >> 2) * 128));   // +64 dims
 #pragma unroll
       for (int rg = 0; rg < NR; ++rg)
         acc[rg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb[rg], acc[rg][db], 0, 0, 0);
@@ -243,7 +346,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     float Ls = 0.f;
     if (M != kNegInf)
       for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
-    f[rg] = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m[rg] - M) / Ls;
+    f[rg] = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m[rg] - M) / Ls * vscale;
   }
   for (int w = 0; w < NW; ++w) {
     if (wave == w) {
@@ -283,28 +386,34 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   }
 }
 
-// Eligible shapes: bf16 DiffKV rows (up to 32 rows per KV head) and bf16 MLA rows (one
-// row group), with a power-of-two block size of at least 16.
+// Eligible shapes: DiffKV rows, bf16 or fp8 (up to 32 rows per KV head), and bf16 MLA
+// rows (one row group), with a power-of-two block size of at least 16.
 static bool dma_is_diffkv(const SplitArgs& a) { return a.c.dk == 192 && a.c.dv == 128 && a.c.v_off == 192; }
 static bool dma_is_mla(const SplitArgs& a) { return a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0; }
+constexpr bool kFp8Nontemporal = true;
+constexpr int kFp8Stages = 3, kFp8MinWaves = 2;   // ring depth; waves per SIMD the registers must allow
 
 bool splitkv_dma_eligible(const SplitArgs& a) {
   const int bs = a.c.block_size;
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int rows = a.max_q * G;
-  if (a.c.esize != 2 || (bs & (bs - 1)) != 0 || bs < sd::TT) return false;
-  return (dma_is_diffkv(a) && rows <= 32) || (dma_is_mla(a) && rows <= 16);
+  if ((bs & (bs - 1)) != 0 || bs < sd::TT) return false;
+  return (dma_is_diffkv(a) && rows <= 32) || (a.c.esize == 2 && dma_is_mla(a) && rows <= 16);
 }
 
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s) {
   dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(sd::NW * 64);
   const int rows = a.max_q * (a.num_q_heads / a.c.num_kv_heads);
   if (dma_is_mla(a))
-    hipLaunchKernelGGL((splitkv_dma_kernel<576, 512, 0, 1, 2, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((splitkv_dma_kernel<576, 512, 0, 1, 2, 1, false, true>), grid, block, 0, s, a);
+  else if (a.c.esize == 1 && rows <= 16)
+    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 1, kFp8Stages, kFp8MinWaves, true, kFp8Nontemporal>), grid, block, 0, s, a);
+  else if (a.c.esize == 1)
+    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 2, kFp8Stages, kFp8MinWaves, true, kFp8Nontemporal>), grid, block, 0, s, a);
   else if (rows <= 16)
-    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 1, 2, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 1, 2, 2, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 2, 2, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((splitkv_dma_kernel<192, 128, 192, 2, 2, 2, false, true>), grid, block, 0, s, a);
 }
 
 }  // namespace pa
