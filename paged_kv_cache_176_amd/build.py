@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "splitkv_wide.hip", "prefill.hip"]
 ARCH = os.environ.get("PAGEDATTN_ARCH", "gfx950")
 
 COMMON_FLAGS = [

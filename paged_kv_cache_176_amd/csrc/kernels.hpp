@@ -43,6 +43,9 @@ struct SplitArgs {
 
 bool splitkv_supported(const SplitArgs& a);
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s);
+// 32-row fp8 variant on 32x32 MFMA tiles (splitkv_wide.hip)
+bool splitkv_wide_eligible(const SplitArgs& a);
+void launch_splitkv_wide(const SplitArgs& a, hipStream_t s);
 // LDS-streamed variant for bf16 rows (splitkv_dma.hip)
 bool splitkv_dma_eligible(const SplitArgs& a);
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s);

@@ -486,6 +486,10 @@ bool splitkv_supported(const SplitArgs& a) {
 }
 
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
+  if (splitkv_wide_eligible(a)) {
+    launch_splitkv_wide(a, s);
+    return true;
+  }
   if (splitkv_dma_eligible(a)) {
     launch_splitkv_dma(a, s);
     return true;
