@@ -7,7 +7,8 @@ keys, 32 query heads over 4 KV heads, K192/V128 bf16, block size 16):
   3. the log-sum-exp merge of its partitions into the bf16 output.
 Inputs are resident in HBM before the timed region.  The step rotates over
 several identical cache copies totalling >= 1 GB, so no step finds its K/V in
-the 256 MB MALL left behind by the previous one.
+the 256 MB MALL left behind by the previous one.  Steps are launched eagerly: a
+HIP graph per cache copy was measured no faster for this three-launch step.
 
 value = algorithmic bytes per step / step time, where the algorithmic bytes are
 the K/V rows read once per (sequence, KV head) plus Q, O and the block table.
@@ -34,25 +35,30 @@ MALL_BYTES = 256 << 20
 
 
 # HBM bytes per launch of the split-KV kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (scaled by a copy of known size), keyed by the sha256 of the kernel source they were
-# taken on: any later change to the kernel reports traffic as null until re-measured.
+# (scaled by a copy of known size), keyed by the sha256 of the kernel's sources and the
+# partition count they were taken at: any later change reports traffic as null until
+# re-measured.
 MEASURED_TRAFFIC = {
-    "5e10c9edba463d8d": 163990.2 * 1024 * 2 + 2176.6 * 1024,
+    ("cb9a81140e70e725", 64): 163984.9 * 1024 * 2 + 1088.0 * 1024,
 }
+KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
 
 
 def _kernel_source_hash():
     import hashlib
-    with open(os.path.join(ROOT, "paged_kv_cache_176_amd", "csrc", "splitkv.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_176_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _copies(nbytes):
     return max(4, math.ceil((1 << 30) / max(1, nbytes)))
 
 
-def auto_partitions(batch, kv_heads, ctx, target_wgs=512, min_keys=256):
-    """Split count: two 4-wave workgroups per CU (512), partitions of >= min_keys keys."""
+def auto_partitions(batch, kv_heads, ctx, target_wgs=256, min_keys=256):
+    """Split count: one 4-wave workgroup per CU (256), partitions of >= min_keys keys."""
     p = max(1, math.ceil(target_wgs / max(1, batch * kv_heads)))
     p = min(p, max(1, ctx // min_keys), 4096)
     return p
@@ -94,6 +100,20 @@ class DecodeCase:
                             sum(math.ceil(int(s) / g.block_size) for s in w.seq_lens.tolist()) * 4)
         # flops: QK^T and PV over every visible key of every query head
         self.flops = 2 * int(w.seq_lens.sum().item()) * Hq * (g.head_dim_k + g.head_dim_v)
+
+    def time_partial(self, reps):
+        """Average duration of the partial kernel alone: reps back-to-back launches (each on
+        the next cache copy) between two HIP events on the launch stream."""
+        import torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            self.pk.decode_splitkv(self.q, self.descs[i % self.ncopy], self.bt, self.seq_lens, self.w.softmax_scale,
+                                   self.P, workspace=self.ws, partials_only=True)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
 
     def step(self, i, ev=None):
         pk = self.pk
@@ -189,10 +209,13 @@ def run_prefill(steps, warmup):
             ev[c][1].record()
 
     dt, _ = time_steps(one, steps, warmup)
-    # per-chunk kernel times from one more instrumented pass
-    one(0, None)
-    torch.cuda.synchronize()
-    kern = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    # per-chunk kernel times: median over instrumented passes
+    passes = []
+    for _ in range(max(3, steps)):
+        one(0, None)
+        torch.cuda.synchronize()
+        passes.append([a.elapsed_time(b) / 1e3 for a, b in ev])
+    kern = [sorted(p[c] for p in passes)[len(passes) // 2] for c in range(T // C)]
     visible = sum((c * C) * C + C * (C + 1) // 2 for c in range(T // C))     # causal pairs per head
     flops = 2 * visible * 32 * (192 + 128)
     return dict(workload="prefill_32768_in_4096_chunks_bs16", ms_per_pass=dt * 1e3, tflops=flops / dt / 1e12,
@@ -234,6 +257,36 @@ def run_verify(mode, steps, warmup, P):
                 kv_gbs=kv / kern / 1e9)
 
 
+def run_mla(batch, steps, warmup):
+    import workloads
+    p = auto_partitions(batch, 1, 100000)
+    c = DecodeCase(workloads.mla_decode(batch, 100000), p)
+    d, k = time_steps(c.step, steps, warmup, events=True)
+    return dict(workload=f"mla_b{batch}_s100000_h12", P=p, us_per_step=round(d * 1e6, 2), kernel_us=round(k * 1e6, 2),
+                kv_gbs=round(c.kv_bytes / k / 1e9, 1), tflops=round(c.flops / k / 1e12, 2))
+
+
+def run_decode_extra(b, s, bs, steps, warmup):
+    import workloads
+    p = auto_partitions(b, 4, s)
+    c = DecodeCase(workloads.long_decode(b, s, bs), p)
+    d, k = time_steps(c.step, steps, warmup, events=True)
+    return dict(workload=f"decode_b{b}_s{s}_bs{bs}", P=p, us_per_step=round(d * 1e6, 2), kernel_us=round(k * 1e6, 2),
+                kv_gbs=round(c.kv_bytes / k / 1e9, 1), step_gbs=round((c.kv_bytes + c.other_bytes) / d / 1e9, 1))
+
+
+def run_only(name, steps, warmup):
+    if name == "prefill":
+        return run_prefill(max(1, min(steps, 5)), max(1, min(warmup, 3)))
+    if name == "fp8_verify":
+        return run_verify("tensor", steps, warmup, auto_partitions(4, 4, 46080))
+    if name == "mla_b1":
+        return run_mla(1, steps, warmup)
+    if name == "mla_b16":
+        return run_mla(16, steps, warmup)
+    return run_decode_extra(8, 8192, 16, steps, warmup)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +295,8 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="split count (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "decode_b8"], default=None,
+                    help="run just this secondary workload and print its JSON line (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
                          "size that calibrates hardware byte counters)")
@@ -256,13 +311,18 @@ def main():
     import workloads
     pk.load_library()
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.only:
+        print(json.dumps(run_only(args.only, args.steps, args.warmup)), flush=True)
+        return
 
     B, S, BS = 1, 131072, 16
     P = args.partitions or auto_partitions(B, 4, S)
     w = workloads.long_decode(B, S, BS)
     case = DecodeCase(w, P)
-    ev_pair = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    dt, kern = time_steps(case.step, args.steps, args.warmup, events=True)
+    # the timed steps, with HIP events around each step's partial kernel; then the partial
+    # kernel alone, launched back to back, for its duration without event overhead
+    dt, kern_in_step = time_steps(case.step, args.steps, args.warmup, events=True)
+    kern = case.time_partial(args.steps)
     algo = case.kv_bytes + case.other_bytes
     value = algo / dt / 1e9
     achieved = case.kv_bytes / kern / 1e9
@@ -285,8 +345,9 @@ def main():
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": MEASURED_TRAFFIC.get(_kernel_source_hash()) if P == 128 else None,
-                     "kernel": "splitkv_partial_kernel<192,128,192,1,bf16,4 waves>", "kernel_us": round(kern * 1e6, 3),
+                     "traffic": MEASURED_TRAFFIC.get((_kernel_source_hash(), P)),
+                     "kernel": "splitkv_dma_kernel<192,128,192,1 row group,2 stages,bf16,nontemporal>",
+                     "kernel_us": round(kern * 1e6, 3), "kernel_us_with_step_events": round(kern_in_step * 1e6, 3),
                      "algorithmic_bytes_per_launch": case.kv_bytes},
     }
     if not args.no_cpu_baseline:
@@ -297,26 +358,14 @@ def main():
     if not args.no_extra:
         extra = {}
         for (b2, s2, bs2) in [(1, 131072, 64), (8, 8192, 16), (8, 8192, 64)]:
-            w2 = workloads.long_decode(b2, s2, bs2)
-            p2 = auto_partitions(b2, 4, s2)
-            c2 = DecodeCase(w2, p2)
-            d2, k2 = time_steps(c2.step, 100, 10, events=True)
-            extra[f"decode_b{b2}_s{s2}_bs{bs2}"] = dict(P=p2, us_per_step=round(d2 * 1e6, 2),
-                                                        kernel_us=round(k2 * 1e6, 2),
-                                                        kv_gbs=round(c2.kv_bytes / k2 / 1e9, 1),
-                                                        step_gbs=round((c2.kv_bytes + c2.other_bytes) / d2 / 1e9, 1))
-            del c2
-        for b2, p2 in [(1, 256), (16, 16)]:
-            w2 = workloads.mla_decode(b2, 100000)
-            c2 = DecodeCase(w2, p2)
-            d2, k2 = time_steps(c2.step, 50, 5, events=True)
-            extra[f"mla_b{b2}_s100000_h12"] = dict(P=p2, us_per_step=round(d2 * 1e6, 2), kernel_us=round(k2 * 1e6, 2),
-                                                   kv_gbs=round(c2.kv_bytes / k2 / 1e9, 1),
-                                                   tflops=round(c2.flops / k2 / 1e12, 2))
-            del c2
+            extra[f"decode_b{b2}_s{s2}_bs{bs2}"] = run_decode_extra(b2, s2, bs2, 100, 10)
+            torch.cuda.empty_cache()
+        for b2 in (1, 16):
+            extra[f"mla_b{b2}_s100000_h12"] = run_mla(b2, 50, 5)
+            torch.cuda.empty_cache()
         for mode in ("tensor", "head"):
-            extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, 64)
-        extra["prefill"] = run_prefill(5, 2)
+            extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, auto_partitions(4, 4, 46080))
+        extra["prefill"] = run_prefill(5, 3)
         line["extra"] = extra
         torch.cuda.empty_cache()
     if args.copy_probe_mib:
