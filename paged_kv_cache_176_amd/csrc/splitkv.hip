@@ -56,7 +56,7 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
   constexpr int VTILE = 16 * VP;     // elements per wave's V tile
   constexpr int MERGE_PITCH = DV + 4;
   constexpr int LDS_V = NW * VTILE * 2;
-  constexpr int LDS_M = NW * ROWS * 2 * 4 + ROWS * MERGE_PITCH * 4;
+  constexpr int LDS_M = NW * ROWS * 2 * 4 + NW * ROWS * MERGE_PITCH * 4;
   constexpr int LDS_BYTES = LDS_V > LDS_M ? LDS_V : LDS_M;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
@@ -295,13 +295,14 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
     }
   }
 
-  // ---- merge the NW waves' states through LDS, fixed order ----
+  // ---- merge the NW waves: each writes its scaled accumulator to its own LDS slab,
+  // then all threads sum the slabs in wave order and write the live rows' partials ----
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) l[rg] = sum_over_groups(l[rg]);
   __syncthreads();                                   // V tiles are dead from here on
   float* mw = reinterpret_cast<float*>(smem);        // [NW][ROWS]
   float* lw = mw + NW * ROWS;                        // [NW][ROWS]
-  float* buf = lw + NW * ROWS;                       // [ROWS][MERGE_PITCH]
+  float* slab = lw + NW * ROWS;                      // [NW][ROWS][MERGE_PITCH]
   if (g == 0) {
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
@@ -321,30 +322,22 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
       for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
     f[rg] = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m[rg] - M) / Ls * vscale;
   }
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
 #pragma unroll
-      for (int rg = 0; rg < NR; ++rg) {
+  for (int rg = 0; rg < NR; ++rg)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          f32x4* dst = reinterpret_cast<f32x4*>(buf + (rg * 16 + n) * MERGE_PITCH + db * 16 + 4 * g);
-          const f32x4 v = acc[rg][db] * f[rg];
-          if (w == 0) *dst = v;
-          else *dst = *dst + v;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // ---- write partials: rows that are live query rows of this sequence ----
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4*>(slab + (wave * ROWS + rg * 16 + n) * MERGE_PITCH + db * 16 + 4 * g) =
+          acc[rg][db] * f[rg];
+  __syncthreads();
   const int64_t Hq = a.num_q_heads;
-  for (int idx = threadIdx.x; idx < ROWS * (DV / 4); idx += NW * 64) {
+  const int live_rows = min(min(L, a.max_q) * G, ROWS);   // row r is live iff r / G < min(L, max_q)
+  for (int idx = threadIdx.x; idx < live_rows * (DV / 4); idx += NW * 64) {
     const int r = idx / (DV / 4), c4 = idx - r * (DV / 4);
     const int qi = r / G, hh = r - qi * G;
-    if (qi >= L || qi >= a.max_q) continue;
     const int64_t tok = q0 + qi, head = kvh * G + hh;
-    float* dst = a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4;
-    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(buf + r * MERGE_PITCH + c4 * 4);
+    f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
+    for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
+    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;
@@ -436,7 +429,7 @@ struct SplitKernel {
   static constexpr int kRows = NR * 16;
   static constexpr int kVTile = 16 * (DV + 16);
   static constexpr int kLdsV = NW * kVTile * 2;
-  static constexpr int kLdsM = NW * kRows * 2 * 4 + kRows * (DV + 4) * 4;
+  static constexpr int kLdsM = NW * kRows * 2 * 4 + NW * kRows * (DV + 4) * 4;
   static constexpr int kLds = kLdsV > kLdsM ? kLdsV : kLdsM;
   static void launch(const SplitArgs& a, hipStream_t s) {
     dim3 grid(a.num_partitions, a.c.num_kv_heads, a.num_seqs), block(NW * 64);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   static_assert(!FP8 || TT * VP * 2 <= TILE_BYTES, "fp8: the bf16 V tile reuses its stage");
   constexpr int MERGE_PITCH = DV + 4;
   constexpr int RING = NW * WAVE_BYTES;
-  constexpr int MERGE = NW * ROWS * 2 * 4 + ROWS * MERGE_PITCH * 4;
+  constexpr int MERGE = NW * ROWS * 2 * 4 + NW * ROWS * MERGE_PITCH * 4;
   constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
   static_assert(CH % (FP8 ? 4 : 8) == 0 && (TT * CH) % 64 == 0, "row must be whole swizzle groups");
   static_assert(!FP8 || (VOFF == DK && DK % 64 == 0 && DV % 64 == 0), "fp8: V follows K, 64-byte pieces");
@@ -88,6 +88,45 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int bs_shift = __builtin_ctz(a.c.block_size);
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+
+  char* ring = smem + wave * WAVE_BYTES;
+  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
+
+  // lane's source offset (bytes from the tile's first row) for DMA instruction u:
+  // 16-byte slot u*64 + lane of the tile holds chunk c of key `key`, swizzled
+  const int ssb = (int)(a.c.ss * ESZ);           // bytes between consecutive slots
+  auto dma_off = [&](int u, int kmax) {
+    const int slot = u * 64 + lane;
+    const int key = slot / CH;
+    const int c = (slot - key * CH) ^ (FP8 ? sd_swz4(key) : sd_swz(key));
+    return min(key, kmax) * ssb + c * 16;
+  };
+  constexpr bool kKeepOff = NINS <= 10;          // precomputed offsets (MLA rows: registers are full)
+  int off[kKeepOff ? NINS : 1];
+#pragma unroll
+  for (int u = 0; u < (kKeepOff ? NINS : 0); ++u) off[u] = dma_off(u, TT - 1);
+
+  auto issue = [&](int ti, int stage) {
+    char* buf = ring + stage * TILE_BYTES;
+    // block_size is a multiple of 16: the tile sits in one block, whose id is
+    // wave-uniform and comes in by a scalar load (lgkmcnt, not the DMA's vmcnt)
+    const int t0 = __builtin_amdgcn_readfirstlane(start + ti * TT);
+    const int64_t blk = load_uniform(btrow + (t0 >> bs_shift));
+    const uint8_t* tile = head_base + (blk * a.c.sb + (int64_t)(t0 & bs_mask) * a.c.ss) * ESZ;
+    const int kmax = end - 1 - t0;                // keys past the partition re-read its last key
+    const bool full = kmax >= TT - 1;
+#pragma unroll
+    for (int u = 0; u < NINS; ++u) {
+      const uint32_t o = (kKeepOff && full) ? off[u] : dma_off(u, kmax);
+      if constexpr (NTL) dma16_nt_s(o, tile, lds_addr(buf + u * 1024));
+      else dma16_s(o, tile, lds_addr(buf + u * 1024));
+    }
+  };
+
+  // the first tiles go out before Q is loaded, so their latency overlaps Q's
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k)
+    if (wave + k * NW < nt) issue(wave + k * NW, k);
 
   // ---- Q rows (B operand), visibility limits ----
   bf16x8 qreg[NR][KS];
@@ -164,42 +203,10 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  char* ring = smem + wave * WAVE_BYTES;
-  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
-  // Q is complete in registers before the first DMA: the explicit vmcnt waits below
-  // count DMA instructions only
+  // Q and the first tiles are complete from here on: the explicit vmcnt waits below
+  // count DMA instructions only, and the compiler, which counts only the loads it
+  // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-
-  // lane's source offset (bytes from the tile's first row) for DMA instruction u:
-  // 16-byte slot u*64 + lane of the tile holds chunk c of key `key`, swizzled
-  const int ssb = (int)(a.c.ss * ESZ);           // bytes between consecutive slots
-  auto dma_off = [&](int u, int kmax) {
-    const int slot = u * 64 + lane;
-    const int key = slot / CH;
-    const int c = (slot - key * CH) ^ (FP8 ? sd_swz4(key) : sd_swz(key));
-    return min(key, kmax) * ssb + c * 16;
-  };
-  constexpr bool kKeepOff = NINS <= 10;          // precomputed offsets (MLA rows: registers are full)
-  int off[kKeepOff ? NINS : 1];
-#pragma unroll
-  for (int u = 0; u < (kKeepOff ? NINS : 0); ++u) off[u] = dma_off(u, TT - 1);
-
-  auto issue = [&](int ti, int stage) {
-    char* buf = ring + stage * TILE_BYTES;
-    // block_size is a multiple of 16: the tile sits in one block, whose id is
-    // wave-uniform and comes in by a scalar load (lgkmcnt, not the DMA's vmcnt)
-    const int t0 = __builtin_amdgcn_readfirstlane(start + ti * TT);
-    const int64_t blk = load_uniform(btrow + (t0 >> bs_shift));
-    const uint8_t* tile = head_base + (blk * a.c.sb + (int64_t)(t0 & bs_mask) * a.c.ss) * ESZ;
-    const int kmax = end - 1 - t0;                // keys past the partition re-read its last key
-    const bool full = kmax >= TT - 1;
-#pragma unroll
-    for (int u = 0; u < NINS; ++u) {
-      const uint32_t o = (kKeepOff && full) ? off[u] : dma_off(u, kmax);
-      if constexpr (NTL) dma16_nt_s(o, tile, lds_addr(buf + u * 1024));
-      else dma16_s(o, tile, lds_addr(buf + u * 1024));
-    }
-  };
 
   auto compute = [&](int ti, int stage) {
     char* buf = ring + stage * TILE_BYTES;
@@ -303,9 +310,6 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 
   // ---- this wave's tiles wave, wave+NW, ...: one consumed while up to NST-1 fly ----
   {
-#pragma unroll
-    for (int k = 0; k < NST - 1; ++k)
-      if (wave + k * NW < nt) issue(wave + k * NW, k);
     int stage = 0;
     for (int ti = wave; ti < nt; ti += NW) {
       const int tn = ti + (NST - 1) * NW;        // tile to start now, into the slot freed last step
@@ -322,13 +326,15 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     }
   }
 
-  // ---- merge the NW waves through LDS in a fixed order, write the partials ----
+  // ---- merge the NW waves: each writes its scaled accumulator to its own LDS slab
+  // (independent stores, no read-modify-write chain), then all threads sum the slabs
+  // in wave order and write the partials of the live rows ----
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) l[rg] = sum_over_groups(l[rg]);
   __syncthreads();                                // rings are dead from here on
-  float* mw = reinterpret_cast<float*>(smem);
-  float* lw = mw + NW * ROWS;
-  float* buf = lw + NW * ROWS;
+  float* mw = reinterpret_cast<float*>(smem);     // [NW][ROWS]
+  float* lw = mw + NW * ROWS;                     // [NW][ROWS]
+  float* slab = lw + NW * ROWS;                   // [NW][ROWS][MERGE_PITCH]
   if (g == 0) {
 #pragma unroll
     for (int rg = 0; rg < NR; ++rg) {
@@ -348,28 +354,22 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
     f[rg] = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m[rg] - M) / Ls * vscale;
   }
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
 #pragma unroll
-      for (int rg = 0; rg < NR; ++rg)
+  for (int rg = 0; rg < NR; ++rg)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          f32x4* dst = reinterpret_cast<f32x4*>(buf + (rg * 16 + n) * MERGE_PITCH + db * 16 + 4 * g);
-          const f32x4 v = acc[rg][db] * f[rg];
-          if (w == 0) *dst = v;
-          else *dst = *dst + v;
-        }
-    }
-    __syncthreads();
-  }
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4*>(slab + (wave * ROWS + rg * 16 + n) * MERGE_PITCH + db * 16 + 4 * g) =
+          acc[rg][db] * f[rg];
+  __syncthreads();
   const int64_t Hq = a.num_q_heads;
-  for (int idx = threadIdx.x; idx < ROWS * (DV / 4); idx += NW * 64) {
+  const int live_rows = min(min(L, a.max_q) * G, ROWS);   // row r is live iff r / G < min(L, max_q)
+  for (int idx = threadIdx.x; idx < live_rows * (DV / 4); idx += NW * 64) {
     const int r = idx / (DV / 4), c4 = idx - r * (DV / 4);
     const int qi = r / G, hh = r - qi * G;
-    if (qi >= L || qi >= a.max_q) continue;
     const int64_t tok = q0 + qi, head = kvh * G + hh;
-    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) =
-        *reinterpret_cast<const f32x4*>(buf + r * MERGE_PITCH + c4 * 4);
+    f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
+    for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
+    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;

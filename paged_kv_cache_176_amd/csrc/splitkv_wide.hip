@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   constexpr int ROWS = 32;
   constexpr int MERGE_PITCH = DV + 4;
   constexpr int RING = NW * NST * TILE_BYTES;
-  constexpr int MERGE = NW * ROWS * 2 * 4 + ROWS * MERGE_PITCH * 4;
+  constexpr int MERGE = NW * ROWS * 2 * 4 + NW * ROWS * MERGE_PITCH * 4;
   constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
 
@@ -83,6 +83,71 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int bs_shift = __builtin_ctz(a.c.block_size);
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+
+  // ---- per-lane LDS offsets ----
+  // K: lane (m = n, g) reads chunk 2j + g of key pi(n); j even/odd differ in bit 1 of
+  // the chunk, the rest of j is an immediate (64 bytes per 4 chunks)
+  const int kkey = sw_pi(n);
+  int koff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) koff[par] = (kkey * CH + sw_pos(2 * par + g, kkey)) * 16;
+  // V (transposing 8-bit read): 16-lane group gi = lane/16 covers dims 16*(gi&1) of a
+  // 32-dim block and keys 8*(gi>>1) of a 16-key half; source lane s of the group
+  // addresses key +(s>>1), bytes 8*(s&1) of its 16-dim chunk
+  int voff[2];
+  {
+    const int gi = lane >> 4, s = lane & 15;
+    const int vkey = 8 * (gi >> 1) + (s >> 1);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      voff[par] = (vkey * CH + sw_pos(12 + 2 * par + (gi & 1), vkey)) * 16 + 8 * (s & 1);
+  }
+  // DMA: slot u*64 + lane of a tile holds chunk (slot % 20) ^ swizzle of key slot / 20;
+  // instructions 0-4 cover keys 0-15, 5-9 keys 16-31 (one 16-key group each)
+  const int ssb = (int)a.c.ss;                   // bytes between consecutive slots (fp8)
+  int dkey[NINS], dbyte[NINS];
+#pragma unroll
+  for (int u = 0; u < NINS; ++u) {
+    const int slot = u * 64 + lane;
+    const int kt = slot / CH;
+    dkey[u] = kt;
+    dbyte[u] = sw_pos(slot - kt * CH, kt) * 16;
+  }
+
+  char* ring = smem + wave * NST * TILE_BYTES;
+  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh;
+
+  auto group_base = [&](int j) {                 // first row of the 16-key group at key j
+    const int64_t blk = load_uniform(btrow + (j >> bs_shift));
+    return head_base + blk * a.c.sb + (int64_t)(j & bs_mask) * a.c.ss;
+  };
+  auto issue = [&](int ti, int stage) {
+    char* buf = ring + stage * TILE_BYTES;
+    const int t0 = __builtin_amdgcn_readfirstlane(start + ti * TT);
+    if (t0 + TT - 1 <= end - 1) {                // whole tile inside the partition
+      const uint8_t* base0 = group_base(t0);
+      const uint8_t* base1 = group_base(t0 + 16);
+#pragma unroll
+      for (int u = 0; u < NINS; ++u)
+        dma16_nt_s((dkey[u] & 15) * ssb + dbyte[u], u < NINS / 2 ? base0 : base1, lds_addr(buf + u * 1024));
+    } else {                                      // keys past the partition re-read its last key
+      const int last = end - 1;
+      const int g0 = t0, g1 = min(t0 + 16, last & ~15);
+      const uint8_t* base0 = group_base(g0);
+      const uint8_t* base1 = group_base(g1);
+#pragma unroll
+      for (int u = 0; u < NINS; ++u) {
+        const int gs = u < NINS / 2 ? g0 : g1;
+        const int j = min(t0 + dkey[u], last);
+        dma16_nt_s((j - gs) * ssb + dbyte[u], u < NINS / 2 ? base0 : base1, lds_addr(buf + u * 1024));
+      }
+    }
+  };
+
+  // the first tiles go out before Q is loaded, so their latency overlaps Q's
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k)
+    if (wave + k * NW < nt) issue(wave + k * NW, k);
 
   // ---- Q row n (B operand): k-step ks holds dims 32(ks/2) + 16g + 8(ks%2) .. +8, the
   // order in which one 16-byte fp8 chunk of K feeds two k-steps ----
@@ -120,36 +185,6 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   for (int o = 1; o < 64; o <<= 1) vis_hi = min(vis_hi, __shfl_xor(vis_hi, o, 64));
   vis_hi = __builtin_amdgcn_readfirstlane(vis_hi);
 
-  // ---- per-lane LDS offsets ----
-  // K: lane (m = n, g) reads chunk 2j + g of key pi(n); j even/odd differ in bit 1 of
-  // the chunk, the rest of j is an immediate (64 bytes per 4 chunks)
-  const int kkey = sw_pi(n);
-  int koff[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) koff[par] = (kkey * CH + sw_pos(2 * par + g, kkey)) * 16;
-  // V (transposing 8-bit read): 16-lane group gi = lane/16 covers dims 16*(gi&1) of a
-  // 32-dim block and keys 8*(gi>>1) of a 16-key half; source lane s of the group
-  // addresses key +(s>>1), bytes 8*(s&1) of its 16-dim chunk
-  int voff[2];
-  {
-    const int gi = lane >> 4, s = lane & 15;
-    const int vkey = 8 * (gi >> 1) + (s >> 1);
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      voff[par] = (vkey * CH + sw_pos(12 + 2 * par + (gi & 1), vkey)) * 16 + 8 * (s & 1);
-  }
-  // DMA: slot u*64 + lane of a tile holds chunk (slot % 20) ^ swizzle of key slot / 20;
-  // instructions 0-4 cover keys 0-15, 5-9 keys 16-31 (one 16-key group each)
-  const int ssb = (int)a.c.ss;                   // bytes between consecutive slots (fp8)
-  int dkey[NINS], dbyte[NINS];
-#pragma unroll
-  for (int u = 0; u < NINS; ++u) {
-    const int slot = u * 64 + lane;
-    const int kt = slot / CH;
-    dkey[u] = kt;
-    dbyte[u] = sw_pos(slot - kt * CH, kt) * 16;
-  }
-
   f32x16 acc[DBW];
 #pragma unroll
   for (int db = 0; db < DBW; ++db)
@@ -157,38 +192,10 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  char* ring = smem + wave * NST * TILE_BYTES;
-  const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh;
-  // Q is complete in registers before the first DMA: the explicit vmcnt waits below
-  // count DMA instructions only
+  // Q and the first tiles are complete from here on: the explicit vmcnt waits below
+  // count DMA instructions only, and the compiler, which counts only the loads it
+  // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-
-  auto group_base = [&](int j) {                 // first row of the 16-key group at key j
-    const int64_t blk = load_uniform(btrow + (j >> bs_shift));
-    return head_base + blk * a.c.sb + (int64_t)(j & bs_mask) * a.c.ss;
-  };
-  auto issue = [&](int ti, int stage) {
-    char* buf = ring + stage * TILE_BYTES;
-    const int t0 = __builtin_amdgcn_readfirstlane(start + ti * TT);
-    if (t0 + TT - 1 <= end - 1) {                // whole tile inside the partition
-      const uint8_t* base0 = group_base(t0);
-      const uint8_t* base1 = group_base(t0 + 16);
-#pragma unroll
-      for (int u = 0; u < NINS; ++u)
-        dma16_nt_s((dkey[u] & 15) * ssb + dbyte[u], u < NINS / 2 ? base0 : base1, lds_addr(buf + u * 1024));
-    } else {                                      // keys past the partition re-read its last key
-      const int last = end - 1;
-      const int g0 = t0, g1 = min(t0 + 16, last & ~15);
-      const uint8_t* base0 = group_base(g0);
-      const uint8_t* base1 = group_base(g1);
-#pragma unroll
-      for (int u = 0; u < NINS; ++u) {
-        const int gs = u < NINS / 2 ? g0 : g1;
-        const int j = min(t0 + dkey[u], last);
-        dma16_nt_s((j - gs) * ssb + dbyte[u], u < NINS / 2 ? base0 : base1, lds_addr(buf + u * 1024));
-      }
-    }
-  };
 
   auto compute = [&](int ti, int stage) {
     const char* buf = ring + stage * TILE_BYTES;
@@ -258,9 +265,6 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
 
   // ---- this wave's tiles wave, wave+NW, ...: one consumed while up to NST-1 fly ----
   {
-#pragma unroll
-    for (int k = 0; k < NST - 1; ++k)
-      if (wave + k * NW < nt) issue(wave + k * NW, k);
     int stage = 0;
     for (int ti = wave; ti < nt; ti += NW) {
       const int tn = ti + (NST - 1) * NW;
@@ -275,7 +279,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     }
   }
 
-  // ---- merge the NW waves through LDS in a fixed order, write the partials ----
+  // ---- merge the NW waves: each writes its scaled accumulator to its own LDS slab
+  // (independent stores, no read-modify-write chain), then all threads sum the slabs
+  // in wave order and write the partials of the live rows ----
   {
     float x = l, y = l;                          // row n's two halves of the keys
     swap_rows32(x, y);
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   __syncthreads();                               // rings are dead from here on
   float* mw = reinterpret_cast<float*>(smem);    // [NW][ROWS]
   float* lw = mw + NW * ROWS;                    // [NW][ROWS]
-  float* buf = lw + NW * ROWS;                   // [ROWS][MERGE_PITCH]
+  float* slab = lw + NW * ROWS;                  // [NW][ROWS][MERGE_PITCH]
   if (g == 0) {
     mw[wave * ROWS + n] = m;
     lw[wave * ROWS + n] = l;
@@ -296,29 +302,22 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   if (M != kNegInf)
     for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + n] * fast_exp2(mw[w * ROWS + n] - M);
   const float f = (M == kNegInf || Ls == 0.f) ? 0.f : fast_exp2(m - M) / Ls * vscale;
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
 #pragma unroll
-      for (int db = 0; db < DBW; ++db)
+  for (int db = 0; db < DBW; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // acc[db][4q + r] is dim 32db + 8q + 4g + r of row n
-          f32x4* dst = reinterpret_cast<f32x4*>(buf + n * MERGE_PITCH + 32 * db + 8 * q + 4 * g);
-          const f32x4 v = f32x4{acc[db][4 * q], acc[db][4 * q + 1], acc[db][4 * q + 2], acc[db][4 * q + 3]} * f;
-          if (w == 0) *dst = v;
-          else *dst = *dst + v;
-        }
-    }
-    __syncthreads();
-  }
+    for (int q = 0; q < 4; ++q)                  // acc[db][4q + r] is dim 32db + 8q + 4g + r of row n
+      *reinterpret_cast<f32x4*>(slab + (wave * ROWS + n) * MERGE_PITCH + 32 * db + 8 * q + 4 * g) =
+          f32x4{acc[db][4 * q], acc[db][4 * q + 1], acc[db][4 * q + 2], acc[db][4 * q + 3]} * f;
+  __syncthreads();
   const int64_t Hq = a.num_q_heads;
-  for (int idx = threadIdx.x; idx < ROWS * (DV / 4); idx += NW * 64) {
+  const int live_rows = min(min(L, a.max_q) * G, ROWS);   // row r is live iff r / G < min(L, max_q)
+  for (int idx = threadIdx.x; idx < live_rows * (DV / 4); idx += NW * 64) {
     const int r = idx / (DV / 4), c4 = idx - r * (DV / 4);
     const int rq = r / G, rh = r - rq * G;
-    if (rq >= L || rq >= a.max_q) continue;
     const int64_t tok = q0 + rq, head = kvh * G + rh;
-    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) =
-        *reinterpret_cast<const f32x4*>(buf + r * MERGE_PITCH + c4 * 4);
+    f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
+    for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
+    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;
