@@ -82,7 +82,7 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 __device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
-               : "v"(src), "s"(lds_base)
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 // Same copy without the nontemporal hint (lines stay in L2 for a neighbour that
@@ -90,7 +90,7 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(lds_base)
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 // Scalar-base forms: address = sbase (wave-uniform, SGPRs) + voff (per lane, 32-bit),
@@ -98,13 +98,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 __device__ __forceinline__ void dma16_nt_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
-               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -415,18 +415,45 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
 
   // keys past the workgroup's last visible key re-read that key: every block id used
   // comes from the staged part of the table (entries 0 .. wg_hi / BS)
+  // Every DMA instruction's 64 lanes lie in one 16-key group (6 K and 4 V
+  // instructions per 16 keys), hence in one block: on full stages the block base is
+  // wave-uniform (SGPRs, from one table entry) and each lane adds a fixed 32-bit
+  // offset, so issuing a stage costs no per-lane 64-bit address arithmetic.
+  const int ss2 = (int)(a.c.ss * 2);
+  const int64_t sb2 = a.c.sb * 2;
+  const int pmask = min(bs_mask, KT - 1);        // in-block position bits a stage can vary
+  int loff[PER_WAVE], ikey[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    loff[u] = (dkey[u] & pmask) * ss2 + dbyte[u];
+    const int slot0 = __builtin_amdgcn_readfirstlane((wave * PER_WAVE + u) * 64);
+    ikey[u] = slot0 < KSLOTS ? slot0 / KCH : (slot0 - KSLOTS) / VCH;   // the instruction's first key
+  }
   auto issue = [&](int st) {
     char* buf = smem + (st % NSTAGE) * STAGE_BYTES;
     const int j0 = st * KT;
     const int kmax = wg_hi - j0;
+    if (kmax >= KT - 1) {
+      const int64_t stage_in_block = (int64_t)(j0 & bs_mask & ~(KT - 1)) * ss2;   // non-zero for BS > 64
+      int blk[PER_WAVE];                          // all table reads first: one LDS wait
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) blk[u] = btl[(j0 + ikey[u]) >> bs_shift];
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const uint8_t* base = head_base + (int64_t)__builtin_amdgcn_readfirstlane(blk[u]) * sb2 + stage_in_block;
+        dma16_s(loff[u], base, lds_addr(buf + (wave * PER_WAVE + u) * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const int j = j0 + min(dkey[u], kmax);
       const int64_t blk = btl[j >> bs_shift];
       const int64_t pos = j & bs_mask;
       const uint8_t* src = head_base + (blk * a.c.sb + pos * a.c.ss) * 2 + dbyte[u];
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (wave * PER_WAVE + u) * 1024),
-                                       16, 0, 0);
+      // inline asm (dma16): the compiler would otherwise answer the LDS-DMA with
+      // vmcnt(0) before some LDS reads; every wait on the ring is explicit
+      dma16(src, lds_addr(buf + (wave * PER_WAVE + u) * 1024));
     }
   };
 
@@ -591,6 +618,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     pv_half(buf, 1, p1);
   };
 
+  // Q is complete from here on.  A wait the compiler sees (the ring's waits are inline
+  // asm, invisible to it): otherwise it assumes Q may still be in flight and answers its
+  // first use on each path with vmcnt(0), which would drain the ring.
+  __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
   // ---- pipeline: stage j is consumed while stages j+1, j+2 are in flight ----
   if (nsteps > 0) issue(0);
   if (nsteps > 1) issue(1);
