@@ -1,9 +1,15 @@
 // Split-KV paged attention: per (partition, KV head, sequence) one workgroup
 // computes the softmax-normalised partial output and log-sum-exp of every query
-// row that uses this KV head, over the partition's key range.
+// row that uses this KV head, over the partition's key range.  This file holds
+// the dispatch (launch_splitkv_partial), the merge kernel and the register-prefetch
+// partial kernel; the shapes that matter most have faster kernels:
+//   splitkv_wide.hip  fp8 DiffKV rows, 17-32 rows per KV head (verify)
+//   splitkv_dma.hip   bf16 DiffKV up to 32 rows, fp8 DiffKV up to 16 rows, bf16 MLA
+//                     (block size a power of two >= 16)
+// and the kernel below serves everything else (other block sizes, 33-64 rows).
 //
-// Serves three shapes with one body (the "rows" of a KV head are its query
-// tokens x its GQA query heads, row r = token_index * G + head_in_group):
+// The "rows" of a KV head are its query tokens x its GQA query heads, row r =
+// token_index * G + head_in_group:
 //   decode  1 token x G heads        (G = 8 for MiMo's 32/4 heads)
 //   verify  L tokens x G heads       (L = 4: 3 drafts + 1, causal among themselves)
 //   MLA     1 token x 12 heads over one 576-wide latent row, V = its first 512
@@ -13,13 +19,14 @@
 // shares one K/V read (diffbot MiMo-V2.6-Flash model card, "Benchmarks" and
 // "What the kernels do").
 //
-// gfx950 mapping (wave64, MFMA):
+// gfx950 mapping of the register-prefetch kernel (wave64, MFMA):
 //   QK^T   S^T[16 keys x 16 rows] += K[16 keys x 32 dims] * Q^T[32 dims x 16 rows]
 //          v_mfma_f32_16x16x32_bf16.  The K operand (lane: key l%16, dims
 //          8*(l/16)..+8) is exactly one 16-byte load of the cache row, so K goes
 //          HBM -> VGPR -> MFMA with no LDS.  Q lives in VGPRs for the whole run.
-//   softmax each lane holds 4 keys of one row; the row max / sum need two
-//          cross-group shuffles.  exp2 with log2(e) folded into the scale.
+//   softmax each lane holds 4 keys of one row; the row max needs two cross-group
+//          exchanges (v_permlane32_swap / v_permlane16_swap).  exp2 with log2(e)
+//          folded into the scale.
 //   PV     O^T[16 dims x 16 rows] += V^T[16 dims x 16 keys] * P^T[16 keys x 16 rows]
 //          v_mfma_f32_16x16x16_bf16.  P^T is the lane's own 4 probabilities
 //          (same lane layout as the S^T output); V^T comes from a per-wave LDS
@@ -27,8 +34,8 @@
 //   fp8 K/V are converted to bf16 in the load path (exact); the K scale is
 //   applied to the fp32 scores, the V scale to the final output.
 // Work split: the workgroup's NW waves take interleaved 16-key tiles of the
-// partition with double-buffered register prefetch, then merge their (m, l,
-// acc) through LDS in a fixed order (deterministic).
+// partition through a ring of 2-3 register buffers, then merge their (m, l, acc)
+// through LDS in a fixed order (deterministic).
 #include "common.hpp"
 #include "kernels.hpp"
 
