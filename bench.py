@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("a8fe703ded362ec1", 64): 163982.1 * 1024 * 2 + 1088.0 * 1024,
+    ("ff33c3e7dd78e31e", 64): 163981.0 * 1024 * 2 + 1088.0 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
 

@@ -107,6 +107,14 @@ __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
+// Wait until at most N vector-memory ops of this wave are in flight (explicit count
+// for the LDS-DMA rings above, which the compiler does not track).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }

@@ -381,8 +381,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   const bool col_ok = c4 * 4 < DV;
   const float* po = a.part_out + rh * P * DV + c4 * 4;
   // this thread's first PRE partials are loaded before the log-sum-exp pass, so that
-  // for P <= PRE * NG the whole merge waits on memory once
-  constexpr int PRE = 4;
+  // for P <= PRE * NG (256 partitions) the whole merge waits on memory once
+  constexpr int PRE = 8;
   f32x4 pre[PRE];
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
@@ -428,6 +428,46 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     *reinterpret_cast<u32x2*>(a.out + rh * DV + c4 * 4) = pk;
   }
   if (a.out_lse && blockIdx.y == 0 && threadIdx.x == 0) a.out_lse[rh] = empty ? kNegInf : M + __builtin_logf(tot);
+}
+
+// Merge for few partitions (P <= PMAX): one thread per (row * Hq + head, float4
+// column), all of its P log-sum-exps and partial float4s loaded at once, no LDS and no
+// barrier.  32 consecutive threads share a row-head (broadcast log-sum-exp loads) and
+// read 512 contiguous bytes of each partial.  Same arithmetic as merge_kernel; the
+// partial sums are added in partition order.
+template <int PMAX>
+__global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
+  const int P = a.num_partitions, DV = a.dv, c4n = a.dv / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (int64_t)a.rows * a.num_q_heads * c4n) return;
+  const int64_t rh = idx / c4n;
+  const int c4 = (int)(idx - rh * c4n);
+  const float* lse = a.part_lse + rh * P;
+  const float* po = a.part_out + rh * P * DV + c4 * 4;
+  float lp[PMAX];
+  f32x4 op[PMAX];
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    lp[p] = p < P ? lse[p] : kNegInf;
+    op[p] = p < P ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) M = fmaxf(M, lp[p]);
+  float tot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != kNegInf) {
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+      const float w = p < P ? fast_exp2((lp[p] - M) * kLog2e) : 0.f;
+      tot += w;
+      acc += op[p] * w;
+    }
+  }
+  const bool empty = (M == kNegInf || tot == 0.f);
+  acc *= empty ? 0.f : 1.0f / tot;
+  *reinterpret_cast<u32x2*>(a.out + rh * DV + c4 * 4) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  if (a.out_lse && c4 == 0) a.out_lse[rh] = empty ? kNegInf : M + __builtin_logf(tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -501,6 +541,13 @@ bool launch_merge(const MergeArgs& a, hipStream_t s) {
   constexpr int NT = 256, SLOTS = 8;
   const int64_t n = (int64_t)a.rows * a.num_q_heads;
   if (n == 0) return true;
+  if (a.num_partitions <= 32 && a.dv % 4 == 0) {
+    const unsigned blocks = (unsigned)((n * (a.dv / 4) + 63) / 64);
+    if (a.num_partitions <= 8) hipLaunchKernelGGL(merge_few_kernel<8>, dim3(blocks), dim3(64), 0, s, a);
+    else if (a.num_partitions <= 16) hipLaunchKernelGGL(merge_few_kernel<16>, dim3(blocks), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(merge_few_kernel<32>, dim3(blocks), dim3(64), 0, s, a);
+    return true;
+  }
   const int slices = (a.dv / 4 + SLOTS - 1) / SLOTS;
   hipLaunchKernelGGL((merge_kernel<NT, SLOTS>), dim3((unsigned)n, slices), dim3(NT),
                      a.num_partitions * sizeof(float), s, a);

@@ -41,13 +41,6 @@ constexpr int TT = 16;                 // keys per tile
 __device__ __forceinline__ int sd_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
 __device__ __forceinline__ int sd_swz4(int key) { return ((key >> 2) ^ (key >> 1)) & 3; }
 
-// wait until at most N vector-memory ops of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // FP8: E4M3FN rows; K chunks are converted to bf16 at the MFMA, V chunks are converted
 // into a per-wave bf16 [key][dim] tile for the transposing read.  NTL: nontemporal DMA.
 template <int DK, int DV, int VOFF, int NR, int NST, int MINW, bool FP8, bool NTL>

@@ -45,12 +45,6 @@ __device__ __forceinline__ int sw_pi(int m) {
   return 16 * (q >> 1) + 8 * gp + 4 * (q & 1) + r;
 }
 
-template <int N>
-__device__ __forceinline__ void sw_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // 8 fp8 bytes (two dwords) -> bf16x8
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const u32x2 a = fp8x4_to_bf16x4(lo), b = fp8x4_to_bf16x4(hi);
@@ -271,9 +265,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
       if (tn < nt) issue(tn, (stage + NST - 1) % NST);
       const int later = min(NST - 1, (nt - 1 - ti) / NW);
       static_assert(NST <= 3, "waits below cover up to 2 tiles in flight");
-      if (NST > 2 && later >= 2) sw_wait_vm<(NST > 2 ? 2 : 0) * NINS>();
-      else if (later >= 1) sw_wait_vm<NINS>();
-      else sw_wait_vm<0>();
+      if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
+      else if (later >= 1) wait_vm<NINS>();
+      else wait_vm<0>();
       compute(ti, stage);
       stage = (stage + 1) % NST;
     }

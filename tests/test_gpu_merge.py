@@ -11,7 +11,10 @@ from oracle import paged_ref as R
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("P,Dv", [(1, 128), (16, 128), (96, 512), (300, 128)])
+# P <= 32 runs the one-thread-per-column kernel (instances for up to 8, 16 and 32
+# partitions), larger P the LDS-combining one
+@pytest.mark.parametrize("P,Dv", [(1, 128), (8, 128), (9, 512), (16, 128), (32, 128), (33, 128), (96, 512),
+                                  (300, 128)])
 def test_merge_matches_oracle(gpu_lib, P, Dv):
     rng = np.random.default_rng(P)
     rows, Hq = 5, 12
