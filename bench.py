@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("ff33c3e7dd78e31e", 64): 163981.0 * 1024 * 2 + 1088.0 * 1024,
+    ("ff33c3e7dd78e31e", 128): 163982.2 * 1024 * 2 + 2176.1 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
 
@@ -57,9 +57,14 @@ def _copies(nbytes):
     return max(4, math.ceil((1 << 30) / max(1, nbytes)))
 
 
-def auto_partitions(batch, kv_heads, ctx, target_wgs=256, min_keys=256):
-    """Split count: one 4-wave workgroup per CU (256), partitions of >= min_keys keys."""
-    p = max(1, math.ceil(target_wgs / max(1, batch * kv_heads)))
+CUS = 256
+
+
+def auto_partitions(batch, kv_heads, ctx, wgs_per_cu=1, min_keys=256):
+    """Split count: as many 4-wave workgroups as the partial kernel keeps resident per CU
+    (two for the bf16 DiffKV decode kernel, one for the MLA and fp8-verify kernels), with
+    partitions of at least min_keys keys."""
+    p = max(1, math.ceil(CUS * wgs_per_cu / max(1, batch * kv_heads)))
     p = min(p, max(1, ctx // min_keys), 4096)
     return p
 
@@ -268,7 +273,7 @@ def run_mla(batch, steps, warmup):
 
 def run_decode_extra(b, s, bs, steps, warmup):
     import workloads
-    p = auto_partitions(b, 4, s)
+    p = auto_partitions(b, 4, s, wgs_per_cu=2)
     c = DecodeCase(workloads.long_decode(b, s, bs), p)
     d, k = time_steps(c.step, steps, warmup, events=True)
     return dict(workload=f"decode_b{b}_s{s}_bs{bs}", P=p, us_per_step=round(d * 1e6, 2), kernel_us=round(k * 1e6, 2),
@@ -316,7 +321,7 @@ def main():
         return
 
     B, S, BS = 1, 131072, 16
-    P = args.partitions or auto_partitions(B, 4, S)
+    P = args.partitions or auto_partitions(B, 4, S, wgs_per_cu=2)
     w = workloads.long_decode(B, S, BS)
     case = DecodeCase(w, P)
     # the timed steps, with HIP events around each step's partial kernel; then the partial
