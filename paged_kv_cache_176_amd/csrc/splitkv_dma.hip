@@ -116,9 +116,11 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     }
   };
 
-  // the first tiles go out before Q is loaded, so their latency overlaps Q's
+  // every stage of the ring is filled before Q is loaded and before the first wait, so
+  // that the opening burst requests NST tiles per wave (a single tile per wave leaves
+  // HBM half idle until the first ones land)
 #pragma unroll
-  for (int k = 0; k < NST - 1; ++k)
+  for (int k = 0; k < NST; ++k)
     if (wave + k * NW < nt) issue(wave + k * NW, k);
 
   // ---- Q rows (B operand), visibility limits ----
@@ -305,8 +307,9 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   {
     int stage = 0;
     for (int ti = wave; ti < nt; ti += NW) {
-      const int tn = ti + (NST - 1) * NW;        // tile to start now, into the slot freed last step
-      if (tn < nt) issue(tn, (stage + NST - 1) % NST);
+      // tile to start now, into the slot freed last step (the first step's came with the prologue)
+      const int tn = ti + (NST - 1) * NW;
+      if (ti != wave && tn < nt) issue(tn, (stage + NST - 1) % NST);
       // tiles issued after ti: min(NST-1, remaining) -> wait until only those are in flight
       const int later = min(NST - 1, (nt - 1 - ti) / NW);
       static_assert(NST <= 4, "waits below cover up to 3 tiles in flight");

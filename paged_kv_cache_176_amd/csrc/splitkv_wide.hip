@@ -138,9 +138,11 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     }
   };
 
-  // the first tiles go out before Q is loaded, so their latency overlaps Q's
+  // every stage of the ring is filled before Q is loaded and before the first wait, so
+  // that the opening burst requests NST tiles per wave (a single tile per wave leaves
+  // HBM half idle until the first ones land)
 #pragma unroll
-  for (int k = 0; k < NST - 1; ++k)
+  for (int k = 0; k < NST; ++k)
     if (wave + k * NW < nt) issue(wave + k * NW, k);
 
   // ---- Q row n (B operand): k-step ks holds dims 32(ks/2) + 16g + 8(ks%2) .. +8, the
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   {
     int stage = 0;
     for (int ti = wave; ti < nt; ti += NW) {
-      const int tn = ti + (NST - 1) * NW;
-      if (tn < nt) issue(tn, (stage + NST - 1) % NST);
+      const int tn = ti + (NST - 1) * NW;        // the first step's tile came with the prologue
+      if (ti != wave && tn < nt) issue(tn, (stage + NST - 1) % NST);
       const int later = min(NST - 1, (nt - 1 - ti) / NW);
       static_assert(NST <= 3, "waits below cover up to 2 tiles in flight");
       if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
