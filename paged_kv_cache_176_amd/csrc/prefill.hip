@@ -589,14 +589,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     f32x16 s0, s1;
     uint32_t p0[8], p1[8];
     qk_half(buf, 0, s0);
-    // region 1: QK of the second half while the first half's softmax runs
+    // region 1: QK of the second half while the first half's softmax runs.  The block
+    // holds both halves' 24 K-operand reads and 24 MFMAs: reads run three MFMAs ahead
+    // (a read issued just before its MFMA exposes a whole LDS round trip per k-step),
+    // and the first half's softmax fills the gaps between the second half's MFMAs.
     qk_half(buf, 1, s1);
     const float a0 = softmax_half(s0, p0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);     // ds_read: operands 0-2
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // ds_read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // mfma
-      __builtin_amdgcn_sched_group_barrier(0x402, 5, 1);   // valu / trans
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // mfma i
+      if (i + 3 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // ds_read i + 3
+      if (i >= KS) __builtin_amdgcn_sched_group_barrier(0x402, 5, 1);          // valu / trans
     }
     if (__any(a0 != 1.0f)) {
 #pragma unroll
@@ -605,10 +609,11 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     // region 2: PV of the first half while the second half's softmax runs
     pv_half(buf, 0, p0);
     const float a1 = softmax_half(s1, p1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);     // ds_read: operands of MFMAs 0-1
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);   // ds_read (two transposed reads)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // mfma
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // mfma i
+      if (i + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);   // two transposed reads, MFMA i + 2
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 2);   // valu / trans
     }
     if (__any(a1 != 1.0f)) {
@@ -616,6 +621,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
       for (int db = 0; db < DB; ++db) acc[db] *= a1;
     }
     pv_half(buf, 1, p1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);     // ds_read: operands of MFMAs 0-1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);   // mfma i
+      if (i + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);   // MFMA i + 2's reads
+    }
   };
 
   // Q is complete from here on.  A wait the compiler sees (the ring's waits are inline
