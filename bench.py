@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("ff33c3e7dd78e31e", 128): 163982.2 * 1024 * 2 + 2176.1 * 1024,
+    ("09ab44ed9cedf6ba", 128): 163989.2 * 1024 * 2 + 2176.2 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
 

@@ -112,14 +112,18 @@ def test_gqa_equals_mha_with_repeated_kv(gpu_lib):
     assert float((lse - lse2).abs().max()) <= 1e-4
 
 
-@pytest.mark.parametrize("shape", [(1, 131072, 16, 64), (1, 131072, 64, 16), (8, 8192, 16, 16), (8, 8192, 64, 32)])
+# the first split of each shape is the one bench.py times (two workgroups per CU), the
+# second another one; both against the same oracle result
+@pytest.mark.parametrize("shape", [(1, 131072, 16, (128, 64)), (1, 131072, 64, (128, 16)), (8, 8192, 16, (16, 8)),
+                                   (8, 8192, 64, (16, 32))])
 def test_long_context_config(gpu_lib, shape):
-    B, S, bs, P = shape
-    log(f"long decode B={B} S={S} bs={bs} P={P}: generating")
+    B, S, bs, Ps = shape
+    log(f"long decode B={B} S={S} bs={bs} P={Ps}: generating")
     w = workloads.long_decode(B, S, bs)
     u = Uploaded(w)
     u.write()
-    out, lse, _ = run_decode(u, P)
+    outs = [run_decode(u, P)[:2] for P in Ps]
     log("oracle")
     ref, ref_lse = oracle_attention(w, u.cache_bytes())
-    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"decode B{B} S{S} bs{bs} P{P}", strict=True)
+    for P, (out, lse) in zip(Ps, outs):
+        compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=f"decode B{B} S{S} bs{bs} P{P}", strict=True)

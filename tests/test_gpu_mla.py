@@ -56,17 +56,22 @@ def test_peaked_mla(gpu_lib):
     assert float(np.abs(ref).max()) > 0.05
 
 
-@pytest.mark.parametrize("B,P", [(1, 96), (16, 32)])
-def test_mla_config(gpu_lib, B, P):
+# the first split of each batch is the one bench.py times
+@pytest.mark.parametrize("B,Ps", [(1, (256, 96)), (16, (16, 32))])
+def test_mla_config(gpu_lib, B, Ps):
     log(f"MLA config B={B}: generating")
     w = workloads.mla_decode(B, 100000)
     u = Uploaded(w)
     u.write()
-    out, lse, _ = run(u, P)
-    out16, lse16, _ = run(u, P, q=padded16(u.q))
-    assert torch.equal(out16[:, :12], out) and torch.equal(lse16[:, :12], lse)
+    outs = {}
+    for P in Ps:
+        out, lse, _ = run(u, P)
+        out16, lse16, _ = run(u, P, q=padded16(u.q))
+        assert torch.equal(out16[:, :12], out) and torch.equal(lse16[:, :12], lse)
+        outs[P] = (out, lse)
     seqs = list(range(B)) if B <= 2 else [0, B // 2, B - 1]
     log(f"oracle on seqs {seqs}")
     ref, ref_lse = oracle_attention(w, u.cache_bytes(), rows=seqs)
     idx = torch.tensor(seqs, device=DEV)
-    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what=f"mla B{B} P{P}", strict=True)
+    for P, (out, lse) in outs.items():
+        compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what=f"mla B{B} P{P}", strict=True)

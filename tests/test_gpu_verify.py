@@ -59,10 +59,11 @@ def test_fp8_verify_config(gpu_lib, mode):
     w = workloads.fp8_verify(scale_mode=mode)
     u = Uploaded(w)
     u.write()
-    out, lse, _ = run_verify(u, 64)
+    outs = {P: run_verify(u, P)[:2] for P in (16, 64)}      # 16: the split bench.py times
     log("oracle")
     ref, ref_lse = oracle_attention(w, u.cache_bytes())
-    compare(out, ref, fp8=True, lse_gpu=lse, lse_ref=ref_lse, what=f"fp8 verify {mode}", strict=True)
-    tail = out[16:].float().cpu()
-    assert torch.all(tail == 0) and not torch.any(torch.signbit(tail))
-    assert torch.all(torch.isneginf(lse[16:].cpu()))
+    for P, (out, lse) in outs.items():
+        compare(out, ref, fp8=True, lse_gpu=lse, lse_ref=ref_lse, what=f"fp8 verify {mode} P{P}", strict=True)
+        tail = out[16:].float().cpu()
+        assert torch.all(tail == 0) and not torch.any(torch.signbit(tail))
+        assert torch.all(torch.isneginf(lse[16:].cpu()))
