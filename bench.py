@@ -307,7 +307,7 @@ def main():
                          "size that calibrates hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
