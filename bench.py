@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("09ab44ed9cedf6ba", 128): 163989.2 * 1024 * 2 + 2176.2 * 1024,
+    ("c868cf39ab00818b", 128): 164006.4 * 1024 * 2 + 2178.7 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
 
@@ -90,6 +90,7 @@ class DecodeCase:
         self.key = w.key.to(dev)
         self.value = w.value.to(dev) if w.value is not None else None
         self.slots = w.slot_mapping.to(dev)
+        assert self.key.shape[0] == w.q.shape[0], "one new token per sequence"
         self.bt = w.block_tables.to(dev)
         self.seq_lens = w.seq_lens.to(dev)
         B, Hq = w.q.shape[0], w.q.shape[1]
@@ -106,6 +107,12 @@ class DecodeCase:
         # flops: QK^T and PV over every visible key of every query head
         self.flops = 2 * int(w.seq_lens.sum().item()) * Hq * (g.head_dim_k + g.head_dim_v)
 
+    def partial(self, d):
+        """The step's first kernel: the new token's write and the split-KV partials
+        (attn_decode_splitkv_append with out=NULL; the write rides in the partial kernel)."""
+        self.pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt, self.seq_lens,
+                                      self.w.softmax_scale, self.P, workspace=self.ws, partials_only=True)
+
     def time_partial(self, reps):
         """Average duration of the partial kernel alone: reps back-to-back launches (each on
         the next cache copy) between two HIP events on the launch stream."""
@@ -114,8 +121,7 @@ class DecodeCase:
         torch.cuda.synchronize()
         e0.record()
         for i in range(reps):
-            self.pk.decode_splitkv(self.q, self.descs[i % self.ncopy], self.bt, self.seq_lens, self.w.softmax_scale,
-                                   self.P, workspace=self.ws, partials_only=True)
+            self.partial(self.descs[i % self.ncopy])
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps / 1e3
@@ -123,14 +129,13 @@ class DecodeCase:
     def step(self, i, ev=None):
         pk = self.pk
         d = self.descs[i % self.ncopy]
-        pk.cache_write(self.key, self.value, self.slots, d)
         if ev is not None:
             ev[0].record()
-        # attn_decode_splitkv with out=NULL (the partial kernel), then attn_merge_lse:
-        # the same two kernels a call with an output buffer enqueues, split so that
-        # the partial kernel can be timed on its own
-        pk.decode_splitkv(self.q, d, self.bt, self.seq_lens, self.w.softmax_scale, self.P, workspace=self.ws,
-                          partials_only=True)
+        # the step: the new token's K/V write and the split-KV partials in one kernel
+        # (attn_decode_splitkv_append with out=NULL), then attn_merge_lse -- the same two
+        # kernels a call with an output buffer enqueues, split so that the partial kernel
+        # can be timed on its own
+        self.partial(d)
         if ev is not None:
             ev[1].record()
         pk.merge_lse(self.po, self.pl, out=self.out, out_lse=self.lse)
@@ -346,7 +351,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"decode_b{B}_s{S}_bs{BS}", "batch": B, "context": S, "q_heads": 32, "kv_heads": 4,
                    "head_dim_k": 192, "head_dim_v": 128, "block_size": BS, "partitions": P,
-                   "cache_copies_rotated": case.ncopy, "step": "cache write of the new token + split-KV partial kernel + merge kernel",
+                   "cache_copies_rotated": case.ncopy, "step": "split-KV partial kernel with the new token's K/V write fused in (attn_decode_splitkv_append) + merge kernel",
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -156,6 +156,35 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
                                 void* out, float* out_lse, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_decode_splitkv_append -- one decode step with its new token: the result
+ * (cache contents, out, out_lse, workspace partials) is that of
+ *   attn_cache_write(key, value, slot_mapping, num_tokens = num_seqs)
+ * followed by attn_decode_splitkv on the same arguments, i.e. the reshape-and-
+ * cache of the step's K/V (vLLM PR #64064, "Details": V with its own head stride
+ * and width) and the split-KV decode that reads it (vLLM PR #50371, review
+ * thread).  Where the decode kernel can take it (power-of-two block size >= 16,
+ * the DiffKV row or the bf16 MLA row, 16-byte aligned sources and strides that are
+ * multiples of 8, value given for DiffKV and NULL for MLA) the write happens inside
+ * the partial kernel: the workgroup whose key range holds key seq_lens[b]-1 writes
+ * row b before reading any key, which saves a launch; otherwise the two kernels
+ * run in that order.
+ *   key / value / slot_mapping: as attn_cache_write, one token per sequence
+ *            (token b belongs to sequence b; value NULL writes K columns only).
+ *   Extra precondition: slot_mapping[b] is -1 or the slot of key seq_lens[b]-1 of
+ *            sequence b (bt[b][(seq_lens[b]-1)/block_size]*block_size +
+ *            (seq_lens[b]-1)%block_size), the decode step's own key.
+ *   All other arguments as attn_decode_splitkv.                              */
+attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
+                                       const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
+                                       const void* key, int64_t key_stride_tok, int64_t key_stride_head,
+                                       const void* value, int64_t val_stride_tok, int64_t val_stride_head,
+                                       const int64_t* slot_mapping,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* out, float* out_lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * attn_merge_lse -- combine split-KV partials.  Per (row, head): M = max_p lse_p;
  * if M = -inf (no partition saw a key) out = 0 and lse = -inf, never NaN (the
  * empty-row fix of the split-KV reducer: diffbot model card, "Update

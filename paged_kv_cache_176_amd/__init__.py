@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     CacheDesc,
     cache_write,
     decode_splitkv,
+    decode_splitkv_append,
     load_library,
     merge_lse,
     prefill_causal,

@@ -89,10 +89,18 @@ size_t splitkv_bytes(int64_t rows, int64_t hq, int64_t dv, int64_t P) {
   return align256(part) + align256(lse);
 }
 
+// New tokens' K/V to write before a decode (attn_decode_splitkv_append).
+struct Append {
+  const void* key; int64_t k_st, k_sh;
+  const void* value; int64_t v_st, v_sh;
+  const int64_t* slots;
+};
+
 attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_sh, const int32_t* qsl,
                         int32_t num_seqs, int32_t rows, int32_t max_q, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
-                        float scale, int32_t P, void* ws, size_t ws_bytes, void* out, float* out_lse, void* stream) {
+                        float scale, int32_t P, void* ws, size_t ws_bytes, void* out, float* out_lse, void* stream,
+                        const Append* app = nullptr) {
   pa::CacheView c;
   attn_status st = make_view(cache, &c, who);
   if (st != ATTN_OK) return st;
@@ -104,6 +112,11 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   if (!std::isfinite(scale)) return fail(ATTN_E_INVALID, "%s: softmax_scale is not finite", who);
   if (rows == 0 || num_seqs == 0) return ATTN_OK;
   if (!q || !bt || !seq_lens || !ws) return fail(ATTN_E_INVALID, "%s: NULL q, block_tables, seq_lens or workspace", who);
+  if (app) {
+    if (!app->key || !app->slots) return fail(ATTN_E_INVALID, "%s: NULL key or slot_mapping", who);
+    if (app->k_st < 0 || app->k_sh < 0 || app->v_st < 0 || app->v_sh < 0)
+      return fail(ATTN_E_INVALID, "%s: negative key/value strides", who);
+  }
   if (bt_stride <= 0) return fail(ATTN_E_INVALID, "%s: bt_stride must be positive", who);
   const size_t need = splitkv_bytes(rows, num_q_heads, c.dv, P);
   if (ws_bytes < need) return fail(ATTN_E_INVALID, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
@@ -128,10 +141,29 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   const size_t part_bytes = align256((size_t)rows * num_q_heads * P * c.dv * sizeof(float));
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes);
   a.rows = rows;
+  a.aslot = nullptr;
+  a.ak = nullptr;
+  a.av = nullptr;
+  a.ak_st = a.ak_sh = a.av_st = a.av_sh = 0;
   if (!pa::splitkv_supported(a))
     return fail(ATTN_E_UNSUPPORTED, "%s: no kernel for head dims %d/%d, v_offset %d, %s cache, %d rows per KV head",
                 who, c.dk, c.dv, c.v_off, c.esize == 1 ? "fp8" : "bf16", max_q * (num_q_heads / c.num_kv_heads));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (app) {
+    a.aslot = app->slots;
+    a.ak = static_cast<const uint16_t*>(app->key);
+    a.ak_st = app->k_st;
+    a.ak_sh = app->k_sh;
+    a.av = static_cast<const uint16_t*>(app->value);
+    a.av_st = app->v_st;
+    a.av_sh = app->v_sh;
+    if (!pa::splitkv_append_fusable(a)) {       // the write as its own kernel, first
+      a.aslot = nullptr;
+      st = attn_cache_write(app->key, app->k_st, app->k_sh, app->value, app->v_st, app->v_sh, app->slots, num_seqs,
+                            cache, stream);
+      if (st != ATTN_OK) return st;
+    }
+  }
   pa::launch_splitkv_partial(a, s);
   st = check_launch(who);
   if (st != ATTN_OK || !out) return st;
@@ -187,6 +219,20 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
   return run_splitkv("attn_decode_splitkv", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
                      num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
                      workspace_bytes, out, out_lse, stream);
+}
+
+attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                       int32_t num_seqs, int32_t num_q_heads, const attn_cache_desc* cache,
+                                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                       float softmax_scale, int32_t num_partitions, const void* key,
+                                       int64_t key_stride_tok, int64_t key_stride_head, const void* value,
+                                       int64_t val_stride_tok, int64_t val_stride_head, const int64_t* slot_mapping,
+                                       void* workspace, size_t workspace_bytes, void* out, float* out_lse,
+                                       void* stream) {
+  const Append app{key, key_stride_tok, key_stride_head, value, val_stride_tok, val_stride_head, slot_mapping};
+  return run_splitkv("attn_decode_splitkv_append", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
+                     num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
+                     workspace_bytes, out, out_lse, stream, &app);
 }
 
 attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const int32_t* query_start_loc,

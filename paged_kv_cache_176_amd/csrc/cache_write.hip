@@ -15,26 +15,6 @@
 
 namespace pa {
 
-// binary32 -> E4M3FN byte: nearest, ties to even, saturating, NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3fn_from_f32(float q) {
-  uint32_t u = __float_as_uint(q);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;                 // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |q| >= 448 or inf: saturate
-  if (a >= 0x3C800000u) {                            // |q| >= 2^-6: normal E4M3FN
-    // keep 3 of the 23 mantissa bits, ties to even on the 20 dropped bits;
-    // a carry out of the mantissa bumps the exponent, as it should
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));         // rebias 127 -> 7
-  }
-  // subnormal range: multiples of 2^-9; |q| * 512 is exact, rint is ties-to-even
-  float m = __builtin_rintf(__builtin_fabsf(q) * 512.0f);
-  return sign | (uint32_t)m;                          // m = 8 is 0x08 = 2^-6, correct
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
 template <bool FP8, bool VEC>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int nk = VEC ? a.c.dk / 8 : a.c.dk;          // vectors (or elements) per head for K
@@ -77,20 +57,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
     } else {
       uint8_t* dst = a.c.data + dst_el;
       if constexpr (VEC) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t w = xv[i];
-          uint32_t b0 = e4m3fn_from_f32(bf16_bits_to_f32(w & 0xFFFFu) / scale);
-          uint32_t b1 = e4m3fn_from_f32(bf16_bits_to_f32(w >> 16) / scale);
-          uint32_t pair = b0 | (b1 << 8);
-          if (i < 2) lo |= pair << (16 * i);
-          else hi |= pair << (16 * (i - 2));
-        }
-        u32x2 o;
-        o[0] = lo;
-        o[1] = hi;
-        *reinterpret_cast<u32x2*>(dst) = o;
+        *reinterpret_cast<u32x2*>(dst) = bf16x8_to_e4m3fn(xv, scale);
       } else {
         *dst = (uint8_t)e4m3fn_from_f32(bf16_bits_to_f32(xs) / scale);
       }

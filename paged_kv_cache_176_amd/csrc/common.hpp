@@ -72,6 +72,41 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// binary32 -> E4M3FN byte: nearest, ties to even, saturating, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3fn_from_f32(float q) {
+  uint32_t u = __float_as_uint(q);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;                 // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |q| >= 448 or inf: saturate
+  if (a >= 0x3C800000u) {                            // |q| >= 2^-6: normal E4M3FN
+    // keep 3 of the 23 mantissa bits, ties to even on the 20 dropped bits;
+    // a carry out of the mantissa bumps the exponent, as it should
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));         // rebias 127 -> 7
+  }
+  // subnormal range: multiples of 2^-9; |q| * 512 is exact, rint is ties-to-even
+  float m = __builtin_rintf(__builtin_fabsf(q) * 512.0f);
+  return sign | (uint32_t)m;                          // m = 8 is 0x08 = 2^-6, correct
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Eight bf16 (one 16-byte vector) -> eight E4M3FN bytes of fp32(x) / scale, in order.
+__device__ __forceinline__ u32x2 bf16x8_to_e4m3fn(u32x4 x, float scale) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = x[i];
+    const uint32_t b0 = e4m3fn_from_f32(bf16_bits_to_f32(w & 0xFFFFu) / scale);
+    const uint32_t b1 = e4m3fn_from_f32(bf16_bits_to_f32(w >> 16) / scale);
+    const uint32_t pair = b0 | (b1 << 8);
+    if (i < 2) lo |= pair << (16 * i);
+    else hi |= pair << (16 * (i - 2));
+  }
+  return u32x2{lo, hi};
+}
+
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4 with the

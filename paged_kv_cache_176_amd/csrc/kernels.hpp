@@ -39,6 +39,12 @@ struct SplitArgs {
   int32_t num_partitions;
   float* part_out; float* part_lse;
   int32_t rows;             // total query rows (tokens)
+  // decode only: token b's new K/V row, written into slot aslot[b] (-1: none) by the
+  // workgroup whose key range holds key seq_len-1, before that workgroup reads any
+  // key.  aslot null: no write.  av null: K columns only (MLA).
+  const int64_t* aslot;
+  const uint16_t* ak; int64_t ak_st, ak_sh;
+  const uint16_t* av; int64_t av_st, av_sh;
 };
 
 bool splitkv_supported(const SplitArgs& a);
@@ -48,6 +54,9 @@ bool splitkv_wide_eligible(const SplitArgs& a);
 void launch_splitkv_wide(const SplitArgs& a, hipStream_t s);
 // LDS-streamed variant for bf16 rows (splitkv_dma.hip)
 bool splitkv_dma_eligible(const SplitArgs& a);
+// the new-token write can ride in the partial kernel (DMA kernel, one query per sequence,
+// 16-byte aligned sources): otherwise the caller launches the cache write first
+bool splitkv_append_fusable(const SplitArgs& a);
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s);
 
 struct MergeArgs {

@@ -82,6 +82,37 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
 
+  // ---- fused new-token write (decode): the workgroup whose key range holds key S-1
+  // (partition 0 when S == 0) writes token b's K/V row of this KV head into its slot and
+  // waits for the stores before any of its waves issues a read; no other workgroup
+  // reads that key ----
+  if (a.aslot) {
+    const int64_t slot = a.aslot[b];
+    const bool mine = S > 0 ? (start <= S - 1 && S - 1 < end) : part == 0;
+    if (mine && slot >= 0) {                     // workgroup-uniform
+      const int nk = DK / 8, nv = a.av ? DV / 8 : 0;
+      const int64_t blk = slot / a.c.block_size;
+      const int64_t row = blk * a.c.sb + (slot - blk * a.c.block_size) * a.c.ss + (int64_t)kvh * a.c.sh;
+      for (int i = threadIdx.x; i < nk + nv; i += NW * 64) {
+        const bool isk = i < nk;
+        const int e0 = (isk ? i : i - nk) * 8;
+        const uint16_t* src = isk ? a.ak + (int64_t)b * a.ak_st + (int64_t)kvh * a.ak_sh + e0
+                                  : a.av + (int64_t)b * a.av_st + (int64_t)kvh * a.av_sh + e0;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        const int64_t el = row + (isk ? 0 : VOFF) + e0;
+        if constexpr (FP8) {
+          const float* sp = isk ? a.c.k_scale : a.c.v_scale;
+          const float sc = a.c.scale_mode == 2 ? sp[kvh] : sp[0];
+          *reinterpret_cast<u32x2*>(a.c.data + el) = bf16x8_to_e4m3fn(x, sc);
+        } else {
+          *reinterpret_cast<u32x4*>(a.c.data + el * 2) = x;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): the row is in L2
+      __syncthreads();
+    }
+  }
+
   char* ring = smem + wave * WAVE_BYTES;
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
 
@@ -395,6 +426,15 @@ bool splitkv_dma_eligible(const SplitArgs& a) {
   const int rows = a.max_q * G;
   if ((bs & (bs - 1)) != 0 || bs < sd::TT) return false;
   return (dma_is_diffkv(a) && rows <= 32) || (a.c.esize == 2 && dma_is_mla(a) && rows <= 16);
+}
+
+bool splitkv_append_fusable(const SplitArgs& a) {
+  auto al = [](const void* p, int n) { return ((uintptr_t)p % n) == 0; };
+  const bool mla = a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0;
+  bool ok = a.qsl == nullptr && splitkv_dma_eligible(a) && al(a.ak, 16) && a.ak_st % 8 == 0 && a.ak_sh % 8 == 0;
+  if (a.av) ok = ok && !mla && al(a.av, 16) && a.av_st % 8 == 0 && a.av_sh % 8 == 0;
+  else ok = ok && mla;                           // a DiffKV row needs its V columns
+  return ok;
 }
 
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s) {

@@ -16,7 +16,8 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 _STATUS = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_HIP"}
 KV_BF16, KV_FP8 = 0, 1
 SCALE_NONE, SCALE_TENSOR, SCALE_HEAD = 0, 1, 2
-EXPORTS = ("attn_cache_write", "attn_splitkv_workspace_bytes", "attn_decode_splitkv", "attn_merge_lse",
+EXPORTS = ("attn_cache_write", "attn_splitkv_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_append",
+           "attn_merge_lse",
            "attn_prefill_causal", "attn_verify", "attn_last_error", "attn_version")
 
 
@@ -66,10 +67,13 @@ def load_library(path: Optional[str] = None):
     lib.attn_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_splitkv_workspace_bytes.restype = sz
     lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.attn_decode_splitkv_append.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32,
+                                               vp, i64, i64, vp, i64, i64, vp, vp, sz, vp, vp, vp]
     lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp]
     lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
-    for name in ("attn_cache_write", "attn_decode_splitkv", "attn_merge_lse", "attn_prefill_causal", "attn_verify"):
+    for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append", "attn_merge_lse",
+                 "attn_prefill_causal", "attn_verify"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.restype = ctypes.c_char_p
@@ -206,6 +210,43 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
     _check(_lib.attn_decode_splitkv(
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
         _ptr(seq_lens), float(softmax_scale), num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+    return out, out_lse, ws
+
+
+def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[torch.Tensor],
+                          slot_mapping: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor,
+                          seq_lens: torch.Tensor, softmax_scale: float, num_partitions: int,
+                          out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, partials_only: bool = False,
+                          with_lse: bool = True, stream=None):
+    """cache_write(key [B, Hkv, Dk], value [B, Hkv, Dv] or None, slot_mapping [B]) followed by
+    decode_splitkv, as one call (the write rides in the decode kernel where it can)."""
+    load_library()
+    _need(q, torch.bfloat16, "q")
+    _need(key, torch.bfloat16, "key")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    if value is not None:
+        _need(value, torch.bfloat16, "value")
+    if key.stride(-1) != 1 or (value is not None and value.stride(-1) != 1):
+        raise ValueError("the last dim of key/value must be contiguous")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq = q.shape[0], q.shape[1]
+    if key.shape[0] != B or slot_mapping.shape[0] != B:
+        raise ValueError("one new token per sequence: key and slot_mapping need num_seqs rows")
+    ws = _workspace(B, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
+    if not partials_only and out is None:
+        out = torch.empty(B, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
+    if not partials_only and with_lse and out_lse is None:
+        out_lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    d = cache.c_struct()
+    _check(_lib.attn_decode_splitkv_append(
+        _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
+        _ptr(seq_lens), float(softmax_scale), num_partitions,
+        _ptr(key), key.stride(0), key.stride(1),
+        _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
+        _ptr(slot_mapping), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
     return out, out_lse, ws
 

@@ -101,6 +101,24 @@ def test_splitkv_argument_checks(lib):
     assert lib.attn_decode_splitkv(*a) == ops.ATTN_E_UNSUPPORTED
 
 
+def test_append_decode_argument_checks(lib):
+    """The write-then-decode call validates its own arguments and the decode's before
+    enqueueing anything (a failing call launches no cache write)."""
+    d = _desc()
+    ws_need = lib.attn_splitkv_workspace_bytes(2, 8, 128, 4)
+    key, slots = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000)
+    args = lambda key, slots, P=4, ks=768: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, 8, ctypes.byref(d),
+                                            ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
+                                            key, ks, 192, ctypes.c_void_p(0x80000), 512, 128, slots,
+                                            ctypes.c_void_p(0x40000), ws_need, ctypes.c_void_p(0x50000), None, None)
+    assert lib.attn_decode_splitkv_append(*args(None, slots)) == ops.ATTN_E_INVALID
+    assert "NULL key or slot_mapping" in lib.attn_last_error().decode()
+    assert lib.attn_decode_splitkv_append(*args(key, None)) == ops.ATTN_E_INVALID
+    assert lib.attn_decode_splitkv_append(*args(key, slots, ks=-1)) == ops.ATTN_E_INVALID
+    assert lib.attn_decode_splitkv_append(*args(key, slots, P=0)) == ops.ATTN_E_INVALID
+    assert "num_partitions" in lib.attn_last_error().decode()
+
+
 def test_merge_and_prefill_argument_checks(lib):
     assert lib.attn_merge_lse(None, None, 1, 8, 128, 4, None, None, None) == ops.ATTN_E_INVALID
     assert lib.attn_merge_lse(None, None, 0, 8, 128, 4, None, None, None) == ops.ATTN_OK
