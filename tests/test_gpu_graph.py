@@ -14,8 +14,9 @@ from _gpu_util import DEV, Uploaded
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_decode_step_graph_replays(gpu_lib, kv):
+def test_decode_step_graph_replays(gpu_lib, kv, append):
     g = workloads.diffkv_geom(0, 16, kv_dtype=kv)
     w = workloads.paged_workload("graph", g, [3000, 517], [1, 1], 32, 1 / math.sqrt(192), seed=41,
                                  scale_mode="none" if kv == "bf16" else "head")
@@ -24,14 +25,21 @@ def test_decode_step_graph_replays(gpu_lib, kv):
     P = 12
     B, Hq = w.q.shape[0], w.q.shape[1]
     key, value, slots = w.key.to(DEV), w.value.to(DEV), w.slot_mapping.to(DEV)
+    if append:                                       # one token per sequence: its last key
+        last = torch.cumsum(w.seq_lens.to(torch.int64), 0) - 1
+        key, value, slots = key[last.to(DEV)], value[last.to(DEV)], slots[last.to(DEV)]
     ws = torch.empty(pk.splitkv_workspace_bytes(B, Hq, g.head_dim_v, P), dtype=torch.uint8, device=DEV)
     po, pl = pk.ops.workspace_views(ws, B, Hq, g.head_dim_v, P)
     out = torch.empty(B, Hq, g.head_dim_v, dtype=torch.bfloat16, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
 
     def step():
-        pk.cache_write(key, value, slots, u.desc)
-        pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, P, workspace=ws, partials_only=True)
+        if append:                                   # the write rides in the partial kernel
+            pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens, w.softmax_scale, P,
+                                     workspace=ws, partials_only=True)
+        else:
+            pk.cache_write(key, value, slots, u.desc)
+            pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, P, workspace=ws, partials_only=True)
         pk.merge_lse(po, pl, out=out, out_lse=lse)
 
     step()
