@@ -103,3 +103,30 @@ def compare(out_gpu: torch.Tensor, ref: np.ndarray, fp8=False, lse_gpu=None, lse
             d = float(np.abs(lg[fin] - lse_ref[fin]).max())
             assert d <= 1e-3, f"{what}: lse err {d}"
     return dict(maxabs=maxabs, rmse=rmse, cos=cos)
+
+
+def split_last_keys(w, u):
+    """For a workload whose cache write covers every key (sequence by sequence): the rows of
+    all keys but each sequence's last (setup), and per sequence the last key's row and slot
+    (a zero row with slot -1 where a sequence has no keys)."""
+    B = w.q.shape[0]
+    lens = w.seq_lens.tolist()
+    assert u.key.shape[0] == sum(lens)
+    last, r = [], 0
+    for s in lens:
+        r += s
+        last.append(r - 1 if s else -1)
+    keep = torch.ones(u.key.shape[0], dtype=torch.bool)
+    keep[[i for i in last if i >= 0]] = False
+    keep = keep.to(DEV)
+    setup = (u.key[keep], u.value[keep] if u.value is not None else None, u.slots[keep])
+    key = torch.zeros(B, *u.key.shape[1:], dtype=torch.bfloat16, device=DEV)
+    value = torch.zeros(B, *u.value.shape[1:], dtype=torch.bfloat16, device=DEV) if u.value is not None else None
+    slots = torch.full((B,), -1, dtype=torch.int64, device=DEV)
+    for b, i in enumerate(last):
+        if i >= 0:
+            key[b] = u.key[i]
+            if value is not None:
+                value[b] = u.value[i]
+            slots[b] = u.slots[i]
+    return setup, (key, value, slots)

@@ -12,36 +12,9 @@ import torch
 
 import paged_kv_cache_176_amd as pk
 import workloads
-from _gpu_util import DEV, Uploaded, compare, oracle_attention
+from _gpu_util import Uploaded, compare, oracle_attention, split_last_keys
 
 pytestmark = pytest.mark.gpu
-
-
-def split_last_keys(w, u):
-    """For a workload whose cache write covers every key (sequence by sequence): the rows of
-    all keys but each sequence's last (setup), and per sequence the last key's row and slot
-    (a zero row with slot -1 where a sequence has no keys)."""
-    B = w.q.shape[0]
-    lens = w.seq_lens.tolist()
-    assert u.key.shape[0] == sum(lens)
-    last, r = [], 0
-    for s in lens:
-        r += s
-        last.append(r - 1 if s else -1)
-    keep = torch.ones(u.key.shape[0], dtype=torch.bool)
-    keep[[i for i in last if i >= 0]] = False
-    keep = keep.to(DEV)
-    setup = (u.key[keep], u.value[keep] if u.value is not None else None, u.slots[keep])
-    key = torch.zeros(B, *u.key.shape[1:], dtype=torch.bfloat16, device=DEV)
-    value = torch.zeros(B, *u.value.shape[1:], dtype=torch.bfloat16, device=DEV) if u.value is not None else None
-    slots = torch.full((B,), -1, dtype=torch.int64, device=DEV)
-    for b, i in enumerate(last):
-        if i >= 0:
-            key[b] = u.key[i]
-            if value is not None:
-                value[b] = u.value[i]
-            slots[b] = u.slots[i]
-    return setup, (key, value, slots)
 
 
 def run_both(w, P):

@@ -1,0 +1,85 @@
+"""Randomised GPU parity sweep: seeded small cases over the shape space each entry point
+serves -- cache dtype and scale granularity, block size (powers of two and not), batch,
+ragged and empty sequences, GQA ratio, query tokens per sequence, split count -- each
+against the oracle on the same cache bytes.  The seeds are fixed; a failing case prints
+its parameters.  Kernel selection differs across these shapes (LDS-streamed, 32-row
+wide and register-prefetch split-KV kernels; fast and generic prefill), so the sweep
+crosses paths the hand-picked tests visit one at a time."""
+import math
+import random
+
+import pytest
+import torch
+
+import paged_kv_cache_176_amd as pk
+import workloads
+from _gpu_util import Uploaded, compare, log, oracle_attention, split_last_keys
+
+pytestmark = pytest.mark.gpu
+
+BLOCK_SIZES = (8, 16, 24, 32, 64)
+
+
+def draw_common(rng):
+    kv = rng.choice(["bf16", "bf16", "fp8"])
+    scales = "none" if kv == "bf16" else rng.choice(["tensor", "head"])
+    bs = rng.choice(BLOCK_SIZES)
+    hkv = rng.choice([1, 2, 4])
+    return kv, scales, bs, hkv
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_split_kv(gpu_lib, seed):
+    rng = random.Random(1000 + seed)
+    kv, scales, bs, hkv = draw_common(rng)
+    G = rng.choice([1, 2, 4, 8, 12, 16])
+    verify = rng.random() < 0.5
+    max_l = max(1, min(8, 64 // G)) if verify else 1
+    B = rng.randint(1, 5)
+    qlens = [rng.randint(1, max_l) for _ in range(B)]
+    lens = [0 if rng.random() < 0.15 else rng.randint(L, 600) for L in qlens]
+    qlens = [L if s else 1 for s, L in zip(lens, qlens)]        # an empty sequence keeps one query row
+    P = rng.choice([1, 2, 3, 7, 16, 33])
+    what = (f"seed {seed}: {'verify' if verify else 'decode'} {kv}/{scales} bs {bs} Hkv {hkv} G {G} "
+            f"lens {lens} L {qlens} P {P}")
+    append = not verify and rng.random() < 0.5     # the decode step's write inside the decode call
+    what += " (append)" if append else ""
+    log(what)
+    g = workloads.diffkv_geom(0, bs, kv_dtype=kv, num_kv_heads=hkv)
+    w = workloads.paged_workload("rand", g, lens, qlens, hkv * G, 1 / math.sqrt(192), seed=seed,
+                                 scale_mode=scales)
+    u = Uploaded(w)
+    if append:
+        setup, (key, value, slots) = split_last_keys(w, u)
+        pk.cache_write(*setup, u.desc)
+        out, lse, _ = pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens, w.softmax_scale,
+                                               P)
+        torch.cuda.synchronize()
+    else:
+        u.write()
+        if verify:
+            out, lse, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, P)
+        else:
+            out, lse, _ = pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, P)
+    ref, ref_lse = oracle_attention(w, u.cache_bytes())
+    compare(out, ref, fp8=kv == "fp8", lse_gpu=lse, lse_ref=ref_lse, what=what)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_prefill(gpu_lib, seed):
+    rng = random.Random(2000 + seed)
+    kv, scales, bs, hkv = draw_common(rng)
+    G = rng.choice([1, 2, 4, 8, 16])
+    B = rng.randint(1, 3)
+    qlens = [rng.randint(1, 200) for _ in range(B)]
+    lens = [L + rng.choice([0, 0, rng.randint(1, 300)]) for L in qlens]   # some chunks follow a context
+    what = f"seed {seed}: prefill {kv}/{scales} bs {bs} Hkv {hkv} G {G} lens {lens} L {qlens}"
+    log(what)
+    g = workloads.diffkv_geom(0, bs, kv_dtype=kv, num_kv_heads=hkv)
+    w = workloads.paged_workload("randpf", g, lens, qlens, hkv * G, 1 / math.sqrt(192), seed=seed,
+                                 scale_mode=scales)
+    u = Uploaded(w)
+    u.write()
+    ref, ref_lse = oracle_attention(w, u.cache_bytes())
+    out, lse = pk.prefill_causal(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len)
+    compare(out, ref, fp8=kv == "fp8", lse_gpu=lse, lse_ref=ref_lse, what=what)
