@@ -94,7 +94,7 @@ class DecodeCase:
         self.bt = w.block_tables.to(dev)
         self.seq_lens = w.seq_lens.to(dev)
         B, Hq = w.q.shape[0], w.q.shape[1]
-        self.ws = torch.empty(pk.splitkv_workspace_bytes(B, Hq, g.head_dim_v, P), dtype=torch.uint8, device=dev)
+        self.ws = pk.new_workspace(B, Hq, g.head_dim_v, P, dev)
         from paged_kv_cache_176_amd.ops import workspace_views
         self.po, self.pl = workspace_views(self.ws, B, Hq, g.head_dim_v, P)
         self.out = torch.empty(B, Hq, g.head_dim_v, dtype=torch.bfloat16, device=dev)
@@ -127,18 +127,17 @@ class DecodeCase:
         return e0.elapsed_time(e1) / reps / 1e3
 
     def step(self, i, ev=None):
-        pk = self.pk
+        """One decode step: attn_decode_splitkv_append with an output buffer -- the new
+        token's K/V write and the split-KV partials in one kernel, then the merge (its own
+        kernel, or folded into the partial kernel where the shape allows)."""
         d = self.descs[i % self.ncopy]
         if ev is not None:
             ev[0].record()
-        # the step: the new token's K/V write and the split-KV partials in one kernel
-        # (attn_decode_splitkv_append with out=NULL), then attn_merge_lse -- the same two
-        # kernels a call with an output buffer enqueues, split so that the partial kernel
-        # can be timed on its own
-        self.partial(d)
+        self.pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt, self.seq_lens,
+                                      self.w.softmax_scale, self.P, out=self.out, out_lse=self.lse,
+                                      workspace=self.ws)
         if ev is not None:
             ev[1].record()
-        pk.merge_lse(self.po, self.pl, out=self.out, out_lse=self.lse)
 
 
 def time_steps(fn, steps, warmup, events=False):
@@ -250,7 +249,7 @@ def run_verify(mode, steps, warmup, P):
     descs = [pk.CacheDesc.from_geom(s, w.geom, ks, vs, mode) for s in copies]
     q, qsl, sl, bt = w.q.to(dev), w.query_start_loc.to(dev), w.seq_lens.to(dev), w.block_tables.to(dev)
     T = q.shape[0]
-    ws = torch.empty(pk.splitkv_workspace_bytes(T, 32, 128, P), dtype=torch.uint8, device=dev)
+    ws = pk.new_workspace(T, 32, 128, P, dev)
     out = torch.empty(T, 32, 128, dtype=torch.bfloat16, device=dev)
 
     def one(i, ev):
@@ -273,8 +272,10 @@ def run_mla(batch, steps, warmup):
     p = auto_partitions(batch, 1, 100000)
     c = DecodeCase(workloads.mla_decode(batch, 100000), p)
     d, _ = time_steps(c.step, steps, warmup)
-    _, k = time_steps(c.step, steps, 0, events=True)
-    return dict(workload=f"mla_b{batch}_s100000_h12", P=p, us_per_step=round(d * 1e6, 2), kernel_us=round(k * 1e6, 2),
+    _, se = time_steps(c.step, steps, 0, events=True)
+    k = c.time_partial(steps)
+    return dict(workload=f"mla_b{batch}_s100000_h12", P=p, us_per_step=round(d * 1e6, 2),
+                step_us_events=round(se * 1e6, 2), partial_kernel_us=round(k * 1e6, 2),
                 kv_gbs=round(c.kv_bytes / k / 1e9, 1), tflops=round(c.flops / k / 1e12, 2))
 
 
@@ -283,8 +284,10 @@ def run_decode_extra(b, s, bs, steps, warmup):
     p = auto_partitions(b, 4, s, wgs_per_cu=2)
     c = DecodeCase(workloads.long_decode(b, s, bs), p)
     d, _ = time_steps(c.step, steps, warmup)
-    _, k = time_steps(c.step, steps, 0, events=True)
-    return dict(workload=f"decode_b{b}_s{s}_bs{bs}", P=p, us_per_step=round(d * 1e6, 2), kernel_us=round(k * 1e6, 2),
+    _, se = time_steps(c.step, steps, 0, events=True)
+    k = c.time_partial(steps)
+    return dict(workload=f"decode_b{b}_s{s}_bs{bs}", P=p, us_per_step=round(d * 1e6, 2),
+                step_us_events=round(se * 1e6, 2), partial_kernel_us=round(k * 1e6, 2),
                 kv_gbs=round(c.kv_bytes / k / 1e9, 1), step_gbs=round((c.kv_bytes + c.other_bytes) / d / 1e9, 1))
 
 
@@ -332,13 +335,13 @@ def main():
     P = args.partitions or auto_partitions(B, 4, S, wgs_per_cu=2)
     w = workloads.long_decode(B, S, BS)
     case = DecodeCase(w, P)
-    # the timed steps (nothing but the step's two kernels between the synchronisations);
-    # then, outside the timed region, the partial kernel alone launched back to back (its
-    # duration for the roofline) and a pass with HIP events around each step's partial
-    # kernel (the per-step figure, which carries the events' own overhead)
+    # the timed steps (nothing but the step's kernels between the synchronisations); then,
+    # outside the timed region, the partial kernel alone launched back to back (its
+    # duration for the roofline) and a pass with HIP events around each step (the per-step
+    # device figure, which carries the events' own overhead)
     dt, _ = time_steps(case.step, args.steps, args.warmup)
     kern = case.time_partial(args.steps)
-    _, kern_in_step = time_steps(case.step, min(args.steps, 50), 0, events=True)
+    _, step_ev = time_steps(case.step, min(args.steps, 50), 0, events=True)
     algo = case.kv_bytes + case.other_bytes
     value = algo / dt / 1e9
     achieved = case.kv_bytes / kern / 1e9
@@ -357,13 +360,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"decode_b{B}_s{S}_bs{BS}", "batch": B, "context": S, "q_heads": 32, "kv_heads": 4,
                    "head_dim_k": 192, "head_dim_v": 128, "block_size": BS, "partitions": P,
-                   "cache_copies_rotated": case.ncopy, "step": "split-KV partial kernel with the new token's K/V write fused in (attn_decode_splitkv_append) + merge kernel",
+                   "cache_copies_rotated": case.ncopy, "step": "attn_decode_splitkv_append: split-KV partial kernel with the new token's K/V write fused in, then the merge",
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": MEASURED_TRAFFIC.get((_kernel_source_hash(), P)),
                      "kernel": "splitkv_dma_kernel<192,128,192,1 row group,2 stages,bf16,nontemporal>",
-                     "kernel_us": round(kern * 1e6, 3), "kernel_us_with_step_events": round(kern_in_step * 1e6, 3),
+                     "kernel_us": round(kern * 1e6, 3), "step_us_with_events": round(step_ev * 1e6, 3),
                      "algorithmic_bytes_per_launch": case.kv_bytes},
     }
     if not args.no_cpu_baseline:

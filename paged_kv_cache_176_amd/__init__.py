@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     decode_splitkv_append,
     load_library,
     merge_lse,
+    new_workspace,
     prefill_causal,
     splitkv_workspace_bytes,
     verify,

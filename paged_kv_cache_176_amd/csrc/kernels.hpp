@@ -54,8 +54,11 @@ bool splitkv_wide_eligible(const SplitArgs& a);
 void launch_splitkv_wide(const SplitArgs& a, hipStream_t s);
 // LDS-streamed variant for bf16 rows (splitkv_dma.hip)
 bool splitkv_dma_eligible(const SplitArgs& a);
-// the new-token write can ride in the partial kernel (DMA kernel, one query per sequence,
-// 16-byte aligned sources): otherwise the caller launches the cache write first
+// the launch runs the LDS-streamed kernel (eligible, and not taken by the 32-row fp8 one)
+bool splitkv_uses_dma(const SplitArgs& a);
+// the new-token write can ride in the partial kernel (the launch runs the DMA kernel, one
+// query per sequence, 16-byte aligned sources): otherwise the caller launches the cache
+// write first
 bool splitkv_append_fusable(const SplitArgs& a);
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s);
 

@@ -525,6 +525,8 @@ bool splitkv_supported(const SplitArgs& a) {
   return dispatch(a, [](auto) {});
 }
 
+bool splitkv_uses_dma(const SplitArgs& a) { return !splitkv_wide_eligible(a) && splitkv_dma_eligible(a); }
+
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
   if (splitkv_wide_eligible(a)) {
     launch_splitkv_wide(a, s);

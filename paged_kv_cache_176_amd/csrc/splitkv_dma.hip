@@ -431,7 +431,7 @@ bool splitkv_dma_eligible(const SplitArgs& a) {
 bool splitkv_append_fusable(const SplitArgs& a) {
   auto al = [](const void* p, int n) { return ((uintptr_t)p % n) == 0; };
   const bool mla = a.c.dk == 576 && a.c.dv == 512 && a.c.v_off == 0;
-  bool ok = a.qsl == nullptr && splitkv_dma_eligible(a) && al(a.ak, 16) && a.ak_st % 8 == 0 && a.ak_sh % 8 == 0;
+  bool ok = a.qsl == nullptr && splitkv_uses_dma(a) && al(a.ak, 16) && a.ak_st % 8 == 0 && a.ak_sh % 8 == 0;
   if (a.av) ok = ok && !mla && al(a.av, 16) && a.av_st % 8 == 0 && a.av_sh % 8 == 0;
   else ok = ok && mla;                           // a DiffKV row needs its V columns
   return ok;

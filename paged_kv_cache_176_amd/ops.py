@@ -174,6 +174,12 @@ def splitkv_workspace_bytes(rows: int, num_q_heads: int, head_dim_v: int, num_pa
     return int(_lib.attn_splitkv_workspace_bytes(rows, num_q_heads, head_dim_v, num_partitions))
 
 
+def new_workspace(rows: int, num_q_heads: int, head_dim_v: int, num_partitions: int, device="cuda") -> torch.Tensor:
+    """A split-KV workspace of the size attn_splitkv_workspace_bytes gives (contents undefined)."""
+    return torch.empty(splitkv_workspace_bytes(rows, num_q_heads, head_dim_v, num_partitions), dtype=torch.uint8,
+                       device=device)
+
+
 def workspace_views(ws: torch.Tensor, rows, num_q_heads, head_dim_v, P):
     """(part_out [rows, Hq, P, Dv], part_lse [rows, Hq, P]) fp32 views of a split-KV workspace."""
     n_out = rows * num_q_heads * P * head_dim_v
@@ -187,7 +193,7 @@ def workspace_views(ws: torch.Tensor, rows, num_q_heads, head_dim_v, P):
 def _workspace(rows, hq, dv, P, device, ws):
     need = splitkv_workspace_bytes(rows, hq, dv, P)
     if ws is None or ws.numel() * ws.element_size() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = new_workspace(rows, hq, dv, P, device)
     return ws
 
 

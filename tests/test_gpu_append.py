@@ -76,3 +76,28 @@ def test_append_partials_and_padding_slot(gpu_lib):
     pa = pk.ops.workspace_views(ws_a, 2, 32, 128, P)
     pb = pk.ops.workspace_views(ws_b, 2, 32, 128, P)
     assert torch.equal(pa[0], pb[0]) and torch.equal(pa[1], pb[1])
+
+
+@pytest.mark.parametrize("G", [24, 32])
+def test_fp8_wide_rows_append(gpu_lib, G):
+    """fp8 decode with more than 16 query heads per KV head runs the 32-row kernel, which
+    does not take the new token's write: the call must launch the write first and give
+    exactly what the separate calls give.  The LDS-streamed kernel's own limits admit these
+    shapes, so the choice of who writes must follow the kernel the launch really runs."""
+    g = workloads.diffkv_geom(0, 16, kv_dtype="fp8", num_kv_heads=1)
+    lens = [600, 17, 0, 33]
+    w = workloads.paged_workload("wide_app", g, lens, [1] * len(lens), G, 1 / math.sqrt(192), seed=94,
+                                 scale_mode="tensor")
+    ua, ub = Uploaded(w), Uploaded(w)
+    setup, (key, value, slots) = split_last_keys(w, ua)
+    for u in (ua, ub):
+        pk.cache_write(*setup, u.desc)
+    pk.cache_write(key, value, slots, ua.desc)
+    P = 5
+    o2, l2, _ = pk.decode_splitkv(ua.q, ua.desc, ua.bt, ua.seq_lens, w.softmax_scale, P)
+    o1, l1, _ = pk.decode_splitkv_append(ub.q, key, value, slots, ub.desc, ub.bt, ub.seq_lens, w.softmax_scale, P)
+    torch.cuda.synchronize()
+    assert torch.equal(ua.storage, ub.storage), "the new token's row was not written"
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref, ref_lse = oracle_attention(w, ub.cache_bytes())
+    compare(o1, ref, fp8=True, lse_gpu=l1, lse_ref=ref_lse, what=f"fp8 G {G} append")

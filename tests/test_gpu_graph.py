@@ -1,7 +1,9 @@
 """A decode step (cache write of the new token, split-KV partials, merge) captured in a
 HIP graph must reproduce the eagerly launched step on every replay, with eager work and
 synchronisations between the replays: the entry points enqueue kernels only (no memset
-nodes, no host synchronisation), so capture records exactly the eager launches."""
+nodes, no host synchronisation), so capture records exactly the eager launches.  The
+"one_call" step is attn_decode_splitkv_append with an output buffer: the library
+enqueues the partial kernel (new-token write inside) and the merge itself."""
 import math
 
 import pytest
@@ -14,9 +16,9 @@ from _gpu_util import DEV, Uploaded
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("append", [False, True])
+@pytest.mark.parametrize("mode", ["separate", "append", "one_call"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_decode_step_graph_replays(gpu_lib, kv, append):
+def test_decode_step_graph_replays(gpu_lib, kv, mode):
     g = workloads.diffkv_geom(0, 16, kv_dtype=kv)
     w = workloads.paged_workload("graph", g, [3000, 517], [1, 1], 32, 1 / math.sqrt(192), seed=41,
                                  scale_mode="none" if kv == "bf16" else "head")
@@ -25,16 +27,20 @@ def test_decode_step_graph_replays(gpu_lib, kv, append):
     P = 12
     B, Hq = w.q.shape[0], w.q.shape[1]
     key, value, slots = w.key.to(DEV), w.value.to(DEV), w.slot_mapping.to(DEV)
-    if append:                                       # one token per sequence: its last key
+    if mode != "separate":                           # one token per sequence: its last key
         last = torch.cumsum(w.seq_lens.to(torch.int64), 0) - 1
         key, value, slots = key[last.to(DEV)], value[last.to(DEV)], slots[last.to(DEV)]
-    ws = torch.empty(pk.splitkv_workspace_bytes(B, Hq, g.head_dim_v, P), dtype=torch.uint8, device=DEV)
+    ws = pk.new_workspace(B, Hq, g.head_dim_v, P, DEV)
     po, pl = pk.ops.workspace_views(ws, B, Hq, g.head_dim_v, P)
     out = torch.empty(B, Hq, g.head_dim_v, dtype=torch.bfloat16, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
 
     def step():
-        if append:                                   # the write rides in the partial kernel
+        if mode == "one_call":                       # write + partials, then the merge: one call
+            pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens, w.softmax_scale, P,
+                                     out=out, out_lse=lse, workspace=ws)
+            return
+        if mode == "append":                         # the write rides in the partial kernel
             pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens, w.softmax_scale, P,
                                      workspace=ws, partials_only=True)
         else:
@@ -60,7 +66,8 @@ def test_decode_step_graph_replays(gpu_lib, kv, append):
     for r in range(4):
         out.zero_()
         lse.fill_(float("nan"))
-        ws.fill_(0xFF)                               # the replay must rewrite every partial it reads
+        po.fill_(float("nan"))                       # the replay must rewrite every partial it reads
+        pl.fill_(float("nan"))
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"replay {r}: output differs from the eager step"
