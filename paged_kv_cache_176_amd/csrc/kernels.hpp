@@ -61,6 +61,10 @@ bool splitkv_uses_dma(const SplitArgs& a);
 // write first
 bool splitkv_append_fusable(const SplitArgs& a);
 void launch_splitkv_dma(const SplitArgs& a, hipStream_t s);
+// bf16 MLA rows with 2 or more query tokens (rows > 16): one wave per token over a
+// shared LDS ring (splitkv_tokens.hip)
+bool splitkv_tokens_eligible(const SplitArgs& a);
+void launch_splitkv_tokens(const SplitArgs& a, hipStream_t s);
 
 struct MergeArgs {
   const float* part_out; const float* part_lse;

@@ -5,7 +5,9 @@
 // partial kernel; the shapes that matter most have faster kernels:
 //   splitkv_wide.hip  fp8 DiffKV rows, 17-32 rows per KV head (verify)
 //   splitkv_dma.hip   bf16 DiffKV up to 32 rows, fp8 DiffKV up to 16 rows, bf16 MLA
-//                     (block size a power of two >= 16)
+//                     up to 16 rows (block size a power of two >= 16)
+//   splitkv_tokens.hip  bf16 MLA with 2 or more query tokens (verify), up to 16 heads
+//                     per KV head (block size a power of two >= 16)
 // and the kernel below serves everything else (other block sizes, 33-64 rows).
 //
 // The "rows" of a KV head are its query tokens x its GQA query heads, row r =
@@ -522,12 +524,16 @@ static bool dispatch(const SplitArgs& a, F&& f) {
 }
 
 bool splitkv_supported(const SplitArgs& a) {
-  return dispatch(a, [](auto) {});
+  return splitkv_tokens_eligible(a) || dispatch(a, [](auto) {});
 }
 
 bool splitkv_uses_dma(const SplitArgs& a) { return !splitkv_wide_eligible(a) && splitkv_dma_eligible(a); }
 
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s) {
+  if (splitkv_tokens_eligible(a)) {
+    launch_splitkv_tokens(a, s);
+    return true;
+  }
   if (splitkv_wide_eligible(a)) {
     launch_splitkv_wide(a, s);
     return true;

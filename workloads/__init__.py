@@ -299,6 +299,14 @@ def fp8_verify(batch=4, ctx=46080, qlen=4, scale_mode="tensor", empty_rows=4, bl
                           extra_empty_rows=empty_rows)
 
 
+def mla_verify(batch, ctx, qlen=4, num_q_heads=12, seed=0, block_size=64):
+    """The MLA decode shape with ``qlen`` query tokens per sequence (drafts + 1), causal
+    among themselves; the older context is placed in the cache image."""
+    g = mla_geom(0, block_size)
+    return paged_workload(f"mla_verify_b{batch}_s{ctx}_l{qlen}_h{num_q_heads}", g, [ctx] * batch, [qlen] * batch,
+                          num_q_heads, 1.0 / math.sqrt(576), seed=seed, std=0.1, write_all=False)
+
+
 def mla_decode(batch, ctx, num_q_heads=12, seed=0, block_size=64):
     """12 q heads on one 576-wide latent head, V = first 512 columns; Q/KV ~ N(0,1)*0.1."""
     g = mla_geom(0, block_size)
