@@ -279,6 +279,44 @@ def run_mla(batch, steps, warmup):
                 kv_gbs=round(c.kv_bytes / k / 1e9, 1), tflops=round(c.flops / k / 1e12, 2))
 
 
+def run_mla_verify(batch, steps, warmup, qlen=4):
+    """MLA verify: qlen query tokens per sequence (drafts + 1) over the 12-head latent
+    cache, S = 100000, rotating cache copies; one attn_verify call (partials, then the merge)."""
+    import torch
+    import paged_kv_cache_176_amd as pk
+    import workloads
+    w = workloads.mla_verify(batch, 100000, qlen=qlen)
+    dev = "cuda:0"
+    img = w.cache_init.clone()
+    workloads.place_bf16_rows(img, w.geom, w.extra["pre_slots"], w.extra["pre_key"], w.extra["pre_value"])
+    nbytes = img.numel() * img.element_size()
+    copies = [img.to(dev) for _ in range(1 if nbytes > 4 * MALL_BYTES else _copies(nbytes))]
+    descs = [pk.CacheDesc.from_geom(c, w.geom) for c in copies]
+    key, slots = w.key.to(dev), w.slot_mapping.to(dev)
+    for d in descs:
+        pk.cache_write(key, None, slots, d)
+    q, qsl, sl, bt = w.q.to(dev), w.query_start_loc.to(dev), w.seq_lens.to(dev), w.block_tables.to(dev)
+    T = q.shape[0]
+    P = auto_partitions(batch, 1, 100000)
+    ws = pk.new_workspace(T, 12, 512, P, dev)
+    out = torch.empty(T, 12, 512, dtype=torch.bfloat16, device=dev)
+
+    def one(i, ev):
+        if ev is not None:
+            ev[0].record()
+        pk.verify(q, qsl, sl, bt, descs[i % len(descs)], w.softmax_scale, qlen, P, out=out, workspace=ws,
+                  with_lse=False)
+        if ev is not None:
+            ev[1].record()
+
+    dt, _ = time_steps(one, steps, warmup)
+    _, kern = time_steps(one, steps, 0, events=True)
+    kv = batch * 100000 * 576 * 2
+    flops = 2 * batch * qlen * 12 * 100000 * (576 + 512)
+    return dict(workload=f"mla_verify_b{batch}_s100000_l{qlen}_h12", P=P, us_per_call=round(dt * 1e6, 2),
+                kernel_us=round(kern * 1e6, 2), kv_gbs=round(kv / dt / 1e9, 1), tflops=round(flops / dt / 1e12, 1))
+
+
 def run_decode_extra(b, s, bs, steps, warmup):
     import workloads
     p = auto_partitions(b, 4, s, wgs_per_cu=2)
@@ -300,6 +338,8 @@ def run_only(name, steps, warmup):
         return run_mla(1, steps, warmup)
     if name == "mla_b16":
         return run_mla(16, steps, warmup)
+    if name == "mla_verify_b16":
+        return run_mla_verify(16, steps, warmup)
     return run_decode_extra(8, 8192, 16, steps, warmup)
 
 
@@ -311,7 +351,7 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="split count (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "decode_b8"], default=None,
+    ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "mla_verify_b16", "decode_b8"], default=None,
                     help="run just this secondary workload and print its JSON line (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
@@ -381,6 +421,9 @@ def main():
             torch.cuda.empty_cache()
         for b2 in (1, 16):
             extra[f"mla_b{b2}_s100000_h12"] = run_mla(b2, 50, 5)
+            torch.cuda.empty_cache()
+        for b2 in (1, 16):
+            extra[f"mla_verify_b{b2}_s100000_l4_h12"] = run_mla_verify(b2, 50, 5)
             torch.cuda.empty_cache()
         for mode in ("tensor", "head"):
             extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, auto_partitions(4, 4, 46080))

@@ -25,11 +25,6 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-command-line-argument",
 ]
-# Per-file flags.  MFMA accumulators in VGPRs: without it the compiler keeps the 512-wide
-# MLA output accumulator in VGPRs for the softmax rescale but runs the MFMAs on AGPR
-# copies, moving all 128 values in and out on every 16-key tile.
-MFMA_IN_VGPRS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-FILE_FLAGS = {"splitkv_tokens.hip": MFMA_IN_VGPRS}
 
 
 def hipcc() -> str:
@@ -41,7 +36,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

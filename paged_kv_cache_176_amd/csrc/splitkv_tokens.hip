@@ -23,7 +23,9 @@
 // tile's direct global->LDS loads are shared by the 4 waves of its half (9 instructions
 // each: a wave's share lies in one 16-key half, hence in one block).  A wave waits for its
 // own share, one workgroup barrier per step publishes the step's tiles and frees the
-// stages of the step before, which the same step refills with step j + 1.
+// stages of the step before, which the same step refills with step j + 1: each wave
+// issues its share between its QK^T and PV MFMAs, so that the 8 waves' loads do not all
+// queue at the barrier and the issue overlaps MFMA work.
 //   QK^T  S^T[16 keys x 16 rows] = K Q^T per 16-key half (two independent MFMA chains),
 //         v_mfma_f32_16x16x32_bf16, K from LDS (ds_read_b128, XOR-swizzled chunks).
 //   PV    O^T[16 dims x 16 rows] += V^T P^T over the 32 keys at once,
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   // not count the DMA, sees this wait and adds none of its own for Q)
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
 
-  auto compute = [&](int k) {
+  // tile k; then, after the QK^T MFMAs, this wave's share of tile kn (kn < 0: none)
+  auto compute = [&](int k, int kn) {
     const char* buf = ring + (k & (NST - 1)) * TILE_BYTES;
     const int j0 = start + k * TT;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[ks], s1, 0, 0, 0);
     }
+    if (kn >= 0) issue(kn);
     // lane (n, g): keys j0 + 4g + i (s0) and j0 + 16 + 4g + i (s1) of row n.  A tile the
     // token sees whole needs no mask, and the scale folds into one fma
     const bool nomask = j0 + TT - 1 <= hi;
@@ -226,8 +230,9 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     if (j >= 2) wait_vm<0>();                      // its share was issued at step j - 1
     __syncthreads();
     const int kn = 2 * (j + 1) + h;
-    if (j >= 1 && kn < nt) issue(kn);
-    if (live && k < nt) compute(k);
+    const bool refill = j >= 1 && kn < nt;
+    if (live && k < nt) compute(k, refill ? kn : -1);
+    else if (refill) issue(kn);
   }
 
   // ---- the token's two halves merge through LDS: half 1 leaves (m, l, acc), half 0
