@@ -109,7 +109,7 @@ def split_last_keys(w, u):
     """For a workload whose cache write covers every key (sequence by sequence): the rows of
     all keys but each sequence's last (setup), and per sequence the last key's row and slot
     (a zero row with slot -1 where a sequence has no keys)."""
-    B = w.q.shape[0]
+    B = w.num_seqs
     lens = w.seq_lens.tolist()
     assert u.key.shape[0] == sum(lens)
     last, r = [], 0

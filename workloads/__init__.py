@@ -53,22 +53,37 @@ class CacheGeom:
     row_dim: int
     kv_dtype: str = "bf16"          # "bf16" or "fp8"
     slack_elems: int = 4096         # guard slack past the cache end
+    # "NHD": [block][slot][head][row] (default); "HND": [block][head][slot][row].  row_pad
+    # widens the pitch between consecutive rows, block_pad the pitch between blocks
+    # (elements; the padding is never read or written).
+    layout: str = "NHD"
+    row_pad: int = 0
+    block_pad: int = 0
 
     @property
     def elem_bytes(self) -> int:
         return 1 if self.kv_dtype == "fp8" else 2
 
     @property
+    def row_pitch(self) -> int:
+        return self.row_dim + self.row_pad
+
+    @property
     def stride_head(self) -> int:
-        return self.row_dim
+        return self.row_pitch if self.layout == "NHD" else self.block_size * self.row_pitch
 
     @property
     def stride_slot(self) -> int:
-        return self.num_kv_heads * self.row_dim
+        return self.num_kv_heads * self.row_pitch if self.layout == "NHD" else self.row_pitch
 
     @property
     def stride_block(self) -> int:
-        return self.block_size * self.num_kv_heads * self.row_dim
+        return self.block_size * self.num_kv_heads * self.row_pitch + self.block_pad
+
+    def rows_view(self, flat: torch.Tensor) -> torch.Tensor:
+        """[num_blocks, block_size, num_kv_heads, row_dim] view of a flat cache image."""
+        return flat.as_strided((self.num_blocks, self.block_size, self.num_kv_heads, self.row_dim),
+                               (self.stride_block, self.stride_slot, self.stride_head, 1))
 
     @property
     def cache_elems(self) -> int:
@@ -79,12 +94,14 @@ class CacheGeom:
         return self.cache_elems + self.slack_elems
 
 
-def diffkv_geom(num_blocks, block_size, kv_dtype="bf16", num_kv_heads=4, slack_elems=4096):
-    return CacheGeom(num_blocks, block_size, num_kv_heads, 192, 128, 192, 320, kv_dtype, slack_elems)
+def diffkv_geom(num_blocks, block_size, kv_dtype="bf16", num_kv_heads=4, slack_elems=4096, layout="NHD",
+                row_pad=0, block_pad=0):
+    return CacheGeom(num_blocks, block_size, num_kv_heads, 192, 128, 192, 320, kv_dtype, slack_elems, layout, row_pad,
+                     block_pad)
 
 
-def mla_geom(num_blocks, block_size=64, slack_elems=4096):
-    return CacheGeom(num_blocks, block_size, 1, 576, 512, 0, 576, "bf16", slack_elems)
+def mla_geom(num_blocks, block_size=64, slack_elems=4096, layout="NHD", row_pad=0, block_pad=0):
+    return CacheGeom(num_blocks, block_size, 1, 576, 512, 0, 576, "bf16", slack_elems, layout, row_pad, block_pad)
 
 
 @dataclass
@@ -147,8 +164,9 @@ def _poisoned_cache(geom: CacheGeom, used_blocks, seq_lens_list, tables) -> torc
     else:
         img = torch.full((geom.total_elems,), BF16_NAN_BITS, dtype=torch.int16)
         poison = int(torch.tensor([BF16_TAIL_POISON], dtype=torch.bfloat16).view(torch.int16).item())
-    view = img[: geom.cache_elems].view(geom.num_blocks, geom.block_size, geom.num_kv_heads, geom.row_dim)
-    # every mapped page starts as finite poison; the write fills the live slots
+    view = geom.rows_view(img)
+    # every mapped page starts as finite poison (its padding stays NaN); the write fills
+    # the live slots
     if len(used_blocks):
         view[torch.as_tensor(used_blocks, dtype=torch.int64)] = poison
     return img
@@ -257,11 +275,12 @@ def place_bf16_rows(cache_img: torch.Tensor, geom: CacheGeom, slots, key, value)
     context predates the measured step; it is not the cache write under test.
     """
     assert geom.kv_dtype == "bf16"
-    view = cache_img[: geom.cache_elems].view(geom.num_blocks * geom.block_size, geom.num_kv_heads, geom.row_dim)
+    view = geom.rows_view(cache_img)
     s = torch.as_tensor(slots, dtype=torch.int64)
-    view[s, :, 0: geom.head_dim_k] = key.view(torch.int16)
+    blk, pos = s // geom.block_size, s % geom.block_size
+    view[blk, pos, :, 0: geom.head_dim_k] = key.view(torch.int16)
     if value is not None:
-        view[s, :, geom.v_offset: geom.v_offset + geom.head_dim_v] = value.view(torch.int16)
+        view[blk, pos, :, geom.v_offset: geom.v_offset + geom.head_dim_v] = value.view(torch.int16)
 
 
 # ---------------------------------------------------------------------------------
