@@ -126,6 +126,18 @@ size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t h
                                     int32_t num_partitions);
 
 /* ---------------------------------------------------------------------------
+ * Sink logits (every attention entry point below takes `sinks`): NULL, or a
+ * device array [num_q_heads] fp32 of per-query-head logits that join every row's
+ * softmax denominator as one extra term with a zero value row (the attention
+ * sink read as an extra softmax-denominator logit: diffbot model card, "Known
+ * issues" on the vision encoder's sink).  In the units of softmax_scale*q.k:
+ *   out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h}),
+ *   lse = ln(sum_j e^{s_j} + e^{sink_h})   (the denominator actually applied).
+ * A row with no visible key then outputs 0 and lse = sink_h.  -inf entries (and
+ * NULL) give exactly the results without a sink.  With split-KV the partials
+ * never include the sink; the merge adds it once.                            */
+
+/* ---------------------------------------------------------------------------
  * attn_decode_splitkv -- one query token per sequence over its paged context.
  * Split-KV (flash-decoding) with a runtime, device-side choice of each
  * partition's key range and a log-sum-exp merge: vLLM PR #50371, review thread
@@ -153,7 +165,7 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
                                 const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                                 const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
                                 void* workspace, size_t workspace_bytes,
-                                void* out, float* out_lse, void* stream);
+                                void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_decode_splitkv_append -- one decode step with its new token: the result
@@ -182,20 +194,21 @@ attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int6
                                        const void* value, int64_t val_stride_tok, int64_t val_stride_head,
                                        const int64_t* slot_mapping,
                                        void* workspace, size_t workspace_bytes,
-                                       void* out, float* out_lse, void* stream);
+                                       void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_merge_lse -- combine split-KV partials.  Per (row, head): M = max_p lse_p;
  * if M = -inf (no partition saw a key) out = 0 and lse = -inf, never NaN (the
  * empty-row fix of the split-KV reducer: diffbot model card, "Update
  * 2026-10-01"); otherwise w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p,
- * lse = M + ln sum w_p.
+ * lse = M + ln sum w_p.  With sinks, sink_h joins as one more partial with
+ * lse = sink_h and a zero output (see "Sink logits").
  *   part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 contiguous;
  *   part_lse [rows, num_q_heads, num_partitions] fp32 contiguous;
  *   out [rows, num_q_heads, head_dim_v] bf16 contiguous; out_lse fp32 or NULL. */
 attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t rows, int32_t num_q_heads,
                            int32_t head_dim_v, int32_t num_partitions,
-                           void* out, float* out_lse, void* stream);
+                           void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_prefill_causal -- causal attention of a batch of query chunks over the
@@ -216,7 +229,7 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
                                 int32_t max_query_len, int32_t num_q_heads,
                                 const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                                 const int32_t* seq_lens, float softmax_scale,
-                                void* out, float* out_lse, void* stream);
+                                void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
  * attn_verify -- speculative-decode verify: a few query tokens per sequence
@@ -228,14 +241,17 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
  * "Benchmarks").  Padded rows (seq_len 0) output exact zeros ("Update
  * 2026-10-01").  Arguments as attn_prefill_causal, plus the split-KV
  * num_partitions and workspace as attn_decode_splitkv (rows = num_tokens).
- * max_query_len * (num_q_heads/num_kv_heads) must be <= 64.                    */
+ * DiffKV rows: max_query_len * (num_q_heads/num_kv_heads) must be <= 64.  The
+ * bf16 MLA latent row: any max_query_len with <= 16 query heads per KV head
+ * (vLLM PR #50371, review thread: the verify that the single-token MLA path
+ * leaves to another kernel).                                                   */
 attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
                         int32_t max_query_len, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                         const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
                         void* workspace, size_t workspace_bytes,
-                        void* out, float* out_lse, void* stream);
+                        void* out, float* out_lse, const float* sinks, void* stream);
 
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* attn_last_error(void);

@@ -15,6 +15,10 @@ Plain definitions, written for checking by eye against the pages:
 * split-KV partials and their merge: the two-stage decode of vLLM PR #50371
   (review thread: split sweep, runtime split count) and the split-KV reducer of
   the diffbot model card; the merge is the log-sum-exp identity.
+* attention sink: a per-query-head logit that joins the softmax denominator as one
+  more term (diffbot model card, "Known issues": the vision encoder's sink read as an
+  extra softmax-denominator logit).  It is taken here as one more key whose score is
+  the sink and whose value row is zero; lse is the log of the whole denominator.
 
 fp8 caches are dequantised as code value x scale (per tensor or per KV head).
 Everything is float64; Q/K/V come in as the exact bf16 / fp8 values.
@@ -133,14 +137,15 @@ def gather_kv(cache_flat: np.ndarray, spec: CacheSpec, block_table_row: np.ndarr
 
 
 def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray, scale: float,
-                   key_range=None):
+                   key_range=None, sinks=None):
     """Softmax attention of query rows of ONE sequence.
 
     q [L, Hq, Dk] float64, K [S, Hkv, Dk], V [S, Hkv, Dv]; query l sits at absolute
     position positions[l] and sees keys j <= positions[l] (restricted to
     ``key_range`` = [lo, hi) when given, for split-KV partials).
     Returns out [L, Hq, Dv] (0 for rows without visible keys) and lse [L, Hq]
-    (natural log, -inf for those rows).
+    (natural log, -inf for those rows).  sinks [Hq] (or None): each head's sink logit
+    is one more score column with a zero value row.
     """
     L, Hq, _ = q.shape
     S, Hkv, Dv = V.shape
@@ -154,6 +159,15 @@ def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.nd
         s = scale * (q[:, h, :] @ K[lo:hi, g, :].T)            # [L, hi-lo]
         visible = keys[None, :] <= np.asarray(positions)[:, None]
         s = np.where(visible, s, -np.inf)
+        if sinks is not None and np.isfinite(sinks[h]):
+            # the sink: one more column, always visible, value row zero
+            s_all = np.concatenate([s, np.full((L, 1), float(sinks[h]))], axis=1)
+            m = s_all.max(axis=1)
+            w = np.exp(s_all - m[:, None])
+            den = w.sum(axis=1)
+            out[:, h, :] = (w[:, :-1] @ V[lo:hi, g, :]) / den[:, None]
+            lse[:, h] = m + np.log(den)
+            continue
         m = s.max(axis=1, initial=-np.inf)
         has = np.isfinite(m)
         w = np.where(visible & has[:, None], np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
@@ -164,7 +178,8 @@ def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.nd
 
 
 def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables, cache_flat: np.ndarray,
-                    spec: CacheSpec, scale: float, k_scale=None, v_scale=None, rows: Optional[Sequence[int]] = None):
+                    spec: CacheSpec, scale: float, k_scale=None, v_scale=None, rows: Optional[Sequence[int]] = None,
+                    sinks=None):
     """Attention of every query token (or of the token ids in ``rows``) over the paged cache.
 
     Query i of sequence b (i < L_b = qsl[b+1] - qsl[b]) sits at position S_b - L_b + i:
@@ -186,7 +201,7 @@ def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables,
         S, L = int(seq_lens[b]), t1 - t0
         K, V = gather_kv(cache_flat, spec, block_tables[b], S, k_scale, v_scale)
         pos = S - L + (want[sel] - t0)
-        o, l = attention_rows(q[want[sel]], K, V, pos, scale)
+        o, l = attention_rows(q[want[sel]], K, V, pos, scale, sinks=sinks)
         out[sel], lse[sel] = o, l
     return out, lse
 
@@ -221,13 +236,19 @@ def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, ca
     return po, pl
 
 
-def merge_lse(part_out: np.ndarray, part_lse: np.ndarray):
+def merge_lse(part_out: np.ndarray, part_lse: np.ndarray, sinks=None):
     """Combine split-KV partials: out = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p - max lse).
 
     A row whose partials are all empty (max lse = -inf) gives out = 0, lse = -inf, never NaN.
+    sinks [Hq] (or None; part_lse is [rows, Hq, P]): each head's sink joins as one more
+    partial whose lse is the sink and whose output is zero.
     """
     po = np.asarray(part_out, dtype=np.float64)
     pl = np.asarray(part_lse, dtype=np.float64)
+    if sinks is not None:
+        sk = np.broadcast_to(np.asarray(sinks, dtype=np.float64)[None, :, None], pl.shape[:-1] + (1,))
+        pl = np.concatenate([pl, sk], axis=-1)
+        po = np.concatenate([po, np.zeros(po.shape[:-2] + (1,) + po.shape[-1:])], axis=-2)
     M = pl.max(axis=-1)
     has = np.isfinite(M)
     Msafe = np.where(has, M, 0.0)

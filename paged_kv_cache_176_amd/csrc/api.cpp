@@ -99,8 +99,8 @@ struct Append {
 attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_sh, const int32_t* qsl,
                         int32_t num_seqs, int32_t rows, int32_t max_q, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
-                        float scale, int32_t P, void* ws, size_t ws_bytes, void* out, float* out_lse, void* stream,
-                        const Append* app = nullptr) {
+                        float scale, int32_t P, void* ws, size_t ws_bytes, void* out, float* out_lse,
+                        const float* sinks, void* stream, const Append* app = nullptr) {
   pa::CacheView c;
   attn_status st = make_view(cache, &c, who);
   if (st != ATTN_OK) return st;
@@ -167,7 +167,7 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   pa::launch_splitkv_partial(a, s);
   st = check_launch(who);
   if (st != ATTN_OK || !out) return st;
-  pa::MergeArgs m{a.part_out, a.part_lse, rows, num_q_heads, c.dv, P, static_cast<uint16_t*>(out), out_lse};
+  pa::MergeArgs m{a.part_out, a.part_lse, rows, num_q_heads, c.dv, P, static_cast<uint16_t*>(out), out_lse, sinks};
   pa::launch_merge(m, s);
   return check_launch(who);
 }
@@ -215,10 +215,10 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
                                 int32_t num_q_heads, const attn_cache_desc* cache, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, float softmax_scale,
                                 int32_t num_partitions, void* workspace, size_t workspace_bytes, void* out,
-                                float* out_lse, void* stream) {
+                                float* out_lse, const float* sinks, void* stream) {
   return run_splitkv("attn_decode_splitkv", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
                      num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
-                     workspace_bytes, out, out_lse, stream);
+                     workspace_bytes, out, out_lse, sinks, stream);
 }
 
 attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
@@ -228,26 +228,27 @@ attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int6
                                        int64_t key_stride_tok, int64_t key_stride_head, const void* value,
                                        int64_t val_stride_tok, int64_t val_stride_head, const int64_t* slot_mapping,
                                        void* workspace, size_t workspace_bytes, void* out, float* out_lse,
-                                       void* stream) {
+                                       const float* sinks, void* stream) {
   const Append app{key, key_stride_tok, key_stride_head, value, val_stride_tok, val_stride_head, slot_mapping};
   return run_splitkv("attn_decode_splitkv_append", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
                      num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
-                     workspace_bytes, out, out_lse, stream, &app);
+                     workspace_bytes, out, out_lse, sinks, stream, &app);
 }
 
 attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const int32_t* query_start_loc,
                         int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                         const int32_t* seq_lens, float softmax_scale, int32_t num_partitions, void* workspace,
-                        size_t workspace_bytes, void* out, float* out_lse, void* stream) {
+                        size_t workspace_bytes, void* out, float* out_lse, const float* sinks, void* stream) {
   if (num_seqs > 0 && !query_start_loc) return fail(ATTN_E_INVALID, "attn_verify: NULL query_start_loc");
   return run_splitkv("attn_verify", q, q_stride_tok, q_stride_head, query_start_loc, num_seqs, num_tokens,
                      max_query_len, num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale,
-                     num_partitions, workspace, workspace_bytes, out, out_lse, stream);
+                     num_partitions, workspace, workspace_bytes, out, out_lse, sinks, stream);
 }
 
 attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t rows, int32_t num_q_heads,
-                           int32_t head_dim_v, int32_t num_partitions, void* out, float* out_lse, void* stream) {
+                           int32_t head_dim_v, int32_t num_partitions, void* out, float* out_lse, const float* sinks,
+                           void* stream) {
   const char* who = "attn_merge_lse";
   if (rows < 0 || num_q_heads <= 0 || head_dim_v <= 0 || num_partitions <= 0)
     return fail(ATTN_E_INVALID, "%s: bad sizes", who);
@@ -257,7 +258,7 @@ attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t
     return fail(ATTN_E_UNSUPPORTED, "%s: %d partitions exceed the merge kernel's limit of 4096", who, num_partitions);
   if (head_dim_v % 4) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim_v must be a multiple of 4", who);
   pa::MergeArgs m{part_out, part_lse, rows, num_q_heads, head_dim_v, num_partitions, static_cast<uint16_t*>(out),
-                  out_lse};
+                  out_lse, sinks};
   pa::launch_merge(m, static_cast<hipStream_t>(stream));
   return check_launch(who);
 }
@@ -266,7 +267,7 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
                                 const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
                                 int32_t max_query_len, int32_t num_q_heads, const attn_cache_desc* cache,
                                 const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
-                                float softmax_scale, void* out, float* out_lse, void* stream) {
+                                float softmax_scale, void* out, float* out_lse, const float* sinks, void* stream) {
   const char* who = "attn_prefill_causal";
   pa::CacheView c;
   attn_status st = make_view(cache, &c, who);
@@ -298,6 +299,7 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
   a.scale = softmax_scale;
   a.out = static_cast<uint16_t*>(out);
   a.out_lse = out_lse;
+  a.sinks = sinks;
   if (!pa::prefill_supported(a))
     return fail(ATTN_E_UNSUPPORTED, "%s: no kernel for head dims %d/%d, v_offset %d, G %d", who, c.dk, c.dv, c.v_off,
                 num_q_heads / c.num_kv_heads);

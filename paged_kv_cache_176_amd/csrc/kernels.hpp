@@ -70,6 +70,7 @@ struct MergeArgs {
   const float* part_out; const float* part_lse;
   int32_t rows, num_q_heads, dv, num_partitions;
   uint16_t* out; float* out_lse;
+  const float* sinks;       // [num_q_heads] extra denominator logits, or null
 };
 bool launch_merge(const MergeArgs& a, hipStream_t s);
 
@@ -81,6 +82,7 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   float scale;
   uint16_t* out; float* out_lse;
+  const float* sinks;       // [num_q_heads] extra denominator logits, or null
 };
 bool prefill_supported(const PrefillArgs& a);
 bool launch_prefill(const PrefillArgs& a, hipStream_t s);

@@ -23,6 +23,23 @@
 
 namespace pa {
 
+// A row's normalisation, with an optional sink logit sk2 (log2 units; -inf: none) that
+// joins the denominator as one more term with a zero value row: denominator
+// l*2^(m-M) + 2^(sk2-M), M = max(m, sk2); num scales the accumulator.  Without a sink
+// this is num/l and m + log2(l) (0 and -inf for a row that saw no key).
+__device__ __forceinline__ void softmax_finish(float m, float l, float sk2, float num, float& inv, float& lse) {
+  if (sk2 == kNegInf) {
+    inv = l > 0.f ? num / l : 0.f;
+    lse = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
+    return;
+  }
+  const float M = fmaxf(m, sk2);
+  const float e0 = l > 0.f ? fast_exp2(m - M) : 0.f;
+  const float den = l * e0 + fast_exp2(sk2 - M);
+  inv = num * e0 / den;
+  lse = (M + __builtin_log2f(den)) * kLn2;
+}
+
 template <int DK, int DV, int VOFF, bool FP8>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = 4;                 // waves
@@ -228,8 +245,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     const int r = rg * 16 + n;
     const int qi = wt0 + r / G, hh = r % G;
     if (qi >= L) continue;
-    const float inv = lt > 0.f ? vscale / lt : 0.f;
     const int64_t tok = q0 + qi, head = kvh * G + hh;
+    float inv, lse;
+    softmax_finish(m[rg], lt, a.sinks ? a.sinks[head] * kLog2e : kNegInf, vscale, inv, lse);
     uint16_t* op = a.out + (tok * a.num_q_heads + head) * DV;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -237,8 +255,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
       u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       *reinterpret_cast<u32x2*>(op + db * 16 + 4 * g) = pk;
     }
-    if (a.out_lse && g == 0)
-      a.out_lse[tok * a.num_q_heads + head] = lt > 0.f ? (m[rg] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+    if (a.out_lse && g == 0) a.out_lse[tok * a.num_q_heads + head] = lse;
   }
 }
 
@@ -652,8 +669,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
   // ---- normalise and write: lane holds dims db*32 + 8q + 4g + 0..3 of its row ----
   const float lt = l + __shfl_xor(l, 32, 64);
   if (live) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int64_t tok = q0 + qi_lane, head = kvh * G + n32 % G;
+    float inv, lse;
+    softmax_finish(m, lt, a.sinks ? a.sinks[head] * kLog2e : kNegInf, 1.0f, inv, lse);
     uint16_t* op = a.out + (tok * a.num_q_heads + head) * DV;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -663,8 +681,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
                     pack_bf16x2(acc[db][4 * qq + 2] * inv, acc[db][4 * qq + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + db * 32 + 8 * qq + 4 * g) = pk;
       }
-    if (a.out_lse && g == 0)
-      a.out_lse[tok * a.num_q_heads + head] = lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : kNegInf;
+    if (a.out_lse && g == 0) a.out_lse[tok * a.num_q_heads + head] = lse;
   }
 }
 

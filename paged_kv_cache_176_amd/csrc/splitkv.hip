@@ -399,6 +399,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __syncthreads();
   float M = kNegInf;
   for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+  const float sk = a.sinks ? a.sinks[rh % a.num_q_heads] : kNegInf;   // sink: one more term, value 0
+  M = fmaxf(M, sk);
   __syncthreads();
   float sum = 0.f;
   for (int p = threadIdx.x; p < P; p += NT) {
@@ -411,6 +413,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
+  tot += sk == kNegInf ? 0.f : fast_exp2((sk - M) * kLog2e);
   const bool empty = (M == kNegInf || tot == 0.f);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -456,6 +459,8 @@ __global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
   float M = kNegInf;
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) M = fmaxf(M, lp[p]);
+  const float sk = a.sinks ? a.sinks[rh % a.num_q_heads] : kNegInf;   // sink: one more term, value 0
+  M = fmaxf(M, sk);
   float tot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (M != kNegInf) {
@@ -466,6 +471,7 @@ __global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
       acc += op[p] * w;
     }
   }
+  tot += sk == kNegInf ? 0.f : fast_exp2((sk - M) * kLog2e);
   const bool empty = (M == kNegInf || tot == 0.f);
   acc *= empty ? 0.f : 1.0f / tot;
   *reinterpret_cast<u32x2*>(a.out + rh * DV + c4 * 4) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};

@@ -66,12 +66,13 @@ def load_library(path: Optional[str] = None):
     lib.attn_cache_write.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, dp, vp]
     lib.attn_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_splitkv_workspace_bytes.restype = sz
-    lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp, vp]
     lib.attn_decode_splitkv_append.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32,
-                                               vp, i64, i64, vp, i64, i64, vp, vp, sz, vp, vp, vp]
-    lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
-    lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp]
-    lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp]
+                                               vp, i64, i64, vp, i64, i64, vp, vp, sz, vp, vp, vp, vp]
+    lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp, vp]
+    lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp,
+                                vp]
     for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append", "attn_merge_lse",
                  "attn_prefill_causal", "attn_verify"):
         getattr(lib, name).restype = ctypes.c_int
@@ -190,6 +191,16 @@ def workspace_views(ws: torch.Tensor, rows, num_q_heads, head_dim_v, P):
     return po, pl
 
 
+def _sinks(sinks: Optional[torch.Tensor], num_q_heads: int):
+    """Device fp32 [num_q_heads] sink logits (or None) -> pointer."""
+    if sinks is None:
+        return None
+    _need(sinks, torch.float32, "sinks")
+    if sinks.numel() != num_q_heads or not sinks.is_contiguous():
+        raise ValueError(f"sinks must be a contiguous [{num_q_heads}] fp32 tensor")
+    return _ptr(sinks)
+
+
 def _workspace(rows, hq, dv, P, device, ws):
     need = splitkv_workspace_bytes(rows, hq, dv, P)
     if ws is None or ws.numel() * ws.element_size() < need:
@@ -200,8 +211,10 @@ def _workspace(rows, hq, dv, P, device, ws):
 def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                    softmax_scale: float, num_partitions: int, out: Optional[torch.Tensor] = None,
                    out_lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   partials_only: bool = False, with_lse: bool = True, stream=None):
-    """One query per sequence: q [B, Hq, Dk] bf16 -> (out [B, Hq, Dv] bf16, lse [B, Hq] fp32, workspace)."""
+                   partials_only: bool = False, with_lse: bool = True, sinks: Optional[torch.Tensor] = None,
+                   stream=None):
+    """One query per sequence: q [B, Hq, Dk] bf16 -> (out [B, Hq, Dv] bf16, lse [B, Hq] fp32, workspace).
+    sinks: optional [Hq] fp32 logits joining each row's softmax denominator (applied by the merge)."""
     load_library()
     _need(q, torch.bfloat16, "q")
     _need(block_tables, torch.int32, "block_tables")
@@ -216,7 +229,8 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
     _check(_lib.attn_decode_splitkv(
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
         _ptr(seq_lens), float(softmax_scale), num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
-        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
+        _stream(stream)))
     return out, out_lse, ws
 
 
@@ -225,7 +239,7 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
                           seq_lens: torch.Tensor, softmax_scale: float, num_partitions: int,
                           out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, partials_only: bool = False,
-                          with_lse: bool = True, stream=None):
+                          with_lse: bool = True, sinks: Optional[torch.Tensor] = None, stream=None):
     """cache_write(key [B, Hkv, Dk], value [B, Hkv, Dv] or None, slot_mapping [B]) followed by
     decode_splitkv, as one call (the write rides in the decode kernel where it can)."""
     load_library()
@@ -253,12 +267,14 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
         _ptr(key), key.stride(0), key.stride(1),
         _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
         _ptr(slot_mapping), _ptr(ws), ws.numel() * ws.element_size(),
-        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
+        _stream(stream)))
     return out, out_lse, ws
 
 
 def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torch.Tensor] = None,
-              out_lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
+              out_lse: Optional[torch.Tensor] = None, with_lse: bool = True, sinks: Optional[torch.Tensor] = None,
+              stream=None):
     """part_out [rows, Hq, P, Dv] fp32, part_lse [rows, Hq, P] fp32 -> (out bf16, lse fp32)."""
     load_library()
     _need(part_out, torch.float32, "part_out")
@@ -271,14 +287,14 @@ def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torc
     if with_lse and out_lse is None:
         out_lse = torch.empty(rows, Hq, dtype=torch.float32, device=part_out.device)
     _check(_lib.attn_merge_lse(_ptr(part_out), _ptr(part_lse), rows, Hq, Dv, P, _ptr(out), _ptr(out_lse),
-                               _stream(stream)))
+                               _sinks(sinks, Hq), _stream(stream)))
     return out, out_lse
 
 
 def prefill_causal(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                    block_tables: torch.Tensor, cache: CacheDesc, softmax_scale: float, max_query_len: int,
                    out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
-                   with_lse: bool = True, stream=None):
+                   with_lse: bool = True, sinks: Optional[torch.Tensor] = None, stream=None):
     load_library()
     _need(q, torch.bfloat16, "q")
     T, Hq = q.shape[0], q.shape[1]
@@ -290,7 +306,7 @@ def prefill_causal(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: tor
     _check(_lib.attn_prefill_causal(
         _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
         ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
-        _ptr(out), _ptr(out_lse), _stream(stream)))
+        _ptr(out), _ptr(out_lse), _sinks(sinks, Hq), _stream(stream)))
     return out, out_lse
 
 
@@ -298,7 +314,7 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
            cache: CacheDesc, softmax_scale: float, max_query_len: int, num_partitions: int,
            out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, partials_only: bool = False, with_lse: bool = True,
-           stream=None):
+           sinks: Optional[torch.Tensor] = None, stream=None):
     load_library()
     _need(q, torch.bfloat16, "q")
     T, Hq = q.shape[0], q.shape[1]
@@ -312,5 +328,6 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
         _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
         ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
         num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
-        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _stream(stream)))
+        None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
+        _stream(stream)))
     return out, out_lse, ws

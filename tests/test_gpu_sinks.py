@@ -1,0 +1,118 @@
+"""GPU parity of the attention sink: per query head, one logit that joins each row's
+softmax denominator with no value (diffbot model card, "Known issues": the sink read as an
+extra softmax-denominator logit).  Split-KV entry points add it in the merge (both merge
+kernels), prefill in its own normalisation (both prefill kernels).  Every path is checked
+against the oracle with the same sinks; -inf sinks must give exactly the no-sink results;
+a sequence without keys outputs 0 and lse = sink."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_176_amd as pk
+import workloads
+from _gpu_util import DEV, Uploaded, compare, oracle_attention, split_last_keys
+from oracle import paged_ref as R
+
+pytestmark = pytest.mark.gpu
+
+
+def sinks_for(hq, seed):
+    g = torch.Generator().manual_seed(seed)
+    s = torch.randn(hq, generator=g, dtype=torch.float32) * 2.0
+    s[1] = -math.inf                                 # one head without a sink
+    return s
+
+
+def oracle_with(w, u, sinks):
+    qb = w.q.view(torch.int16).numpy().view(np.uint16)
+    ks = w.k_scale.numpy() if w.k_scale is not None else None
+    vs = w.v_scale.numpy() if w.v_scale is not None else None
+    return R.paged_attention(qb, w.query_start_loc.numpy(), w.seq_lens.numpy(), w.block_tables.numpy(),
+                             u.cache_bytes(), R.CacheSpec.from_geom(w.geom), w.softmax_scale, ks, vs,
+                             sinks=sinks.double().numpy())
+
+
+@pytest.mark.parametrize("kv,scales", [("bf16", "none"), ("fp8", "head")])
+def test_decode_verify_prefill_with_sinks(gpu_lib, kv, scales):
+    g = workloads.diffkv_geom(0, 16, kv_dtype=kv)
+    lens, qlens = [700, 0, 130, 33], [4, 1, 2, 1]
+    w = workloads.paged_workload("sinks", g, lens, qlens, 32, 1 / math.sqrt(192), seed=97, scale_mode=scales)
+    u = Uploaded(w)
+    u.write()
+    sk = sinks_for(32, 1)
+    skd = sk.to(DEV)
+    ref, ref_lse = oracle_with(w, u, sk)
+    fp8 = kv == "fp8"
+    for P in (1, 5, 40):                              # merge_few (P <= 32) and merge_kernel
+        out, lse, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, P,
+                                sinks=skd)
+        compare(out, ref, fp8=fp8, lse_gpu=lse, lse_ref=ref_lse, what=f"verify {kv} P {P} with sinks")
+        o0, l0, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, P)
+        o1, l1, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, P,
+                              sinks=torch.full((32,), -math.inf, device=DEV))
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), "-inf sinks differ from no sinks"
+    # the empty sequence (token 4): zeros and lse = sink
+    e = int(w.query_start_loc[1].item())
+    assert torch.all(out[e].float() == 0)
+    assert torch.equal(lse[e].cpu(), sk)
+    # prefill chunks (every query sees its own key): both prefill kernels normalise with the sink
+    w = workloads.paged_workload("sinks_pf", g, [300, 130, 33], [120, 64, 33], 32, 1 / math.sqrt(192), seed=101,
+                                 scale_mode=scales)
+    u = Uploaded(w)
+    u.write()
+    ref, ref_lse = oracle_with(w, u, sk)
+    out, lse = pk.prefill_causal(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, sinks=skd)
+    compare(out, ref, fp8=fp8, lse_gpu=lse, lse_ref=ref_lse, what=f"prefill {kv} with sinks")
+    o0, l0 = pk.prefill_causal(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len)
+    o1, l1 = pk.prefill_causal(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len,
+                               sinks=torch.full((32,), -math.inf, device=DEV))
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_decode_and_append_with_sinks(gpu_lib):
+    g = workloads.diffkv_geom(0, 16)
+    lens = [900, 17, 0, 260]
+    w = workloads.paged_workload("sinks_dec", g, lens, [1] * 4, 32, 1 / math.sqrt(192), seed=98)
+    ua, ub = Uploaded(w), Uploaded(w)
+    setup, (key, value, slots) = split_last_keys(w, ua)
+    for u in (ua, ub):
+        pk.cache_write(*setup, u.desc)
+    pk.cache_write(key, value, slots, ua.desc)
+    sk = sinks_for(32, 2)
+    skd = sk.to(DEV)
+    o1, l1, _ = pk.decode_splitkv(ua.q, ua.desc, ua.bt, ua.seq_lens, w.softmax_scale, 7, sinks=skd)
+    o2, l2, _ = pk.decode_splitkv_append(ub.q, key, value, slots, ub.desc, ub.bt, ub.seq_lens, w.softmax_scale, 7,
+                                         sinks=skd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref, ref_lse = oracle_with(w, ua, sk)
+    compare(o1, ref, lse_gpu=l1, lse_ref=ref_lse, what="decode with sinks")
+
+
+def test_merge_lse_with_sinks(gpu_lib):
+    """The merge entry point alone, on the oracle's own partials (exact fp32 inputs)."""
+    rows, hq, P, dv = 5, 8, 9, 128
+    g = torch.Generator().manual_seed(99)
+    po = torch.randn(rows, hq, P, dv, generator=g) * 0.01    # attention-sized outputs (the bf16 bounds)
+    pl = torch.randn(rows, hq, P, generator=g) * 3
+    pl[0, :, :] = -math.inf                          # a row that saw no key
+    pl[2, 3, 4:] = -math.inf
+    sk = sinks_for(hq, 3)
+    mo, ml = R.merge_lse(po.double().numpy(), pl.double().numpy(), sinks=sk.double().numpy())
+    out, lse = pk.merge_lse(po.to(DEV), pl.to(DEV), sinks=sk.to(DEV))
+    compare(out, mo, lse_gpu=lse, lse_ref=ml, what="merge with sinks")
+    assert torch.all(out[0].float() == 0) and torch.equal(lse[0].cpu(), sk)
+
+
+def test_mla_verify_with_sinks(gpu_lib):
+    w = workloads.paged_workload("sinks_mla", workloads.mla_geom(0, 64), [2000, 70], [4, 3], 12,
+                                 1 / math.sqrt(576), seed=100, std=0.1)
+    u = Uploaded(w)
+    u.write()
+    sk = sinks_for(12, 4) * 0.1
+    out, lse, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, 8,
+                            sinks=sk.to(DEV))
+    ref, ref_lse = oracle_with(w, u, sk)
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what="MLA verify with sinks")

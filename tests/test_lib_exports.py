@@ -87,7 +87,8 @@ def test_splitkv_argument_checks(lib):
     assert lib.attn_splitkv_workspace_bytes(-1, 8, 128, 4) == 0
     args = lambda P, ws_bytes, hq=8: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, hq, ctypes.byref(d),
                                       ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
-                                      ctypes.c_void_p(0x40000), ws_bytes, ctypes.c_void_p(0x50000), None, None)
+                                      ctypes.c_void_p(0x40000), ws_bytes, ctypes.c_void_p(0x50000), None, None,
+                                      None)
     assert lib.attn_decode_splitkv(*args(0, ws_need)) == ops.ATTN_E_INVALID
     assert lib.attn_decode_splitkv(*args(5000, ws_need)) == ops.ATTN_E_INVALID
     assert lib.attn_decode_splitkv(*args(4, ws_need - 1)) == ops.ATTN_E_INVALID
@@ -110,7 +111,8 @@ def test_append_decode_argument_checks(lib):
     args = lambda key, slots, P=4, ks=768: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, 8, ctypes.byref(d),
                                             ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
                                             key, ks, 192, ctypes.c_void_p(0x80000), 512, 128, slots,
-                                            ctypes.c_void_p(0x40000), ws_need, ctypes.c_void_p(0x50000), None, None)
+                                            ctypes.c_void_p(0x40000), ws_need, ctypes.c_void_p(0x50000), None, None,
+                                            None)
     assert lib.attn_decode_splitkv_append(*args(None, slots)) == ops.ATTN_E_INVALID
     assert "NULL key or slot_mapping" in lib.attn_last_error().decode()
     assert lib.attn_decode_splitkv_append(*args(key, None)) == ops.ATTN_E_INVALID
@@ -120,16 +122,17 @@ def test_append_decode_argument_checks(lib):
 
 
 def test_merge_and_prefill_argument_checks(lib):
-    assert lib.attn_merge_lse(None, None, 1, 8, 128, 4, None, None, None) == ops.ATTN_E_INVALID
-    assert lib.attn_merge_lse(None, None, 0, 8, 128, 4, None, None, None) == ops.ATTN_OK
+    assert lib.attn_merge_lse(None, None, 1, 8, 128, 4, None, None, None, None) == ops.ATTN_E_INVALID
+    assert lib.attn_merge_lse(None, None, 0, 8, 128, 4, None, None, None, None) == ops.ATTN_OK
     assert lib.attn_merge_lse(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 1, 8, 128, 5000,
-                              ctypes.c_void_p(1 << 22), None, None) == ops.ATTN_E_UNSUPPORTED
+                              ctypes.c_void_p(1 << 22), None, None, None) == ops.ATTN_E_UNSUPPORTED
     d = _desc()
-    st = lib.attn_prefill_causal(None, 0, 0, None, 1, 4, 4, 8, ctypes.byref(d), None, 1, None, 0.1, None, None, None)
+    st = lib.attn_prefill_causal(None, 0, 0, None, 1, 4, 4, 8, ctypes.byref(d), None, 1, None, 0.1, None, None, None,
+                                 None)
     assert st == ops.ATTN_E_INVALID
     st = lib.attn_prefill_causal(ctypes.c_void_p(0x1000), 8 * 192, 192, ctypes.c_void_p(0x2000), 1, 4, 4, 8,
                                  ctypes.byref(d), ctypes.c_void_p(0x3000), 1, ctypes.c_void_p(0x4000),
-                                 float("nan"), ctypes.c_void_p(0x5000), None, None)
+                                 float("nan"), ctypes.c_void_p(0x5000), None, None, None)
     assert st == ops.ATTN_E_INVALID and "not finite" in lib.attn_last_error().decode()
 
 
