@@ -90,6 +90,24 @@ typedef struct {
   const float* v_scale; /* device, [1] or [num_kv_heads]; NULL iff scale_mode NONE */
 } attn_cache_desc;
 
+/* Split policy: how many of a launch's num_partitions a sequence actually uses,
+ * chosen on the device from its seq_len by context buckets, so that the launch
+ * shape stays fixed (graph-stable) while short and long contexts get their own
+ * split count, and the partial and merge kernels read the same table (vLLM PR
+ * #50371, review thread: active splits derived from device-side sequence lengths
+ * in both stages, context buckets -- e.g. 96 for a 100K context -- and the wish
+ * for one table shared by the two stages).  Bucket i holds seq_len <=
+ * max_seq_len[i] (ascending); a longer sequence takes the last bucket.  A
+ * sequence uses min(splits[i], num_partitions) partitions of ceil(seq_len /
+ * that) keys (rounded up to the 16-key tile); the others are empty.  The table is
+ * read on the host at the call and travels by value with the launch.          */
+#define ATTN_MAX_SPLIT_BUCKETS 8
+typedef struct {
+  int32_t num_buckets;                          /* 0..8; 0: all partitions active  */
+  int32_t max_seq_len[ATTN_MAX_SPLIT_BUCKETS];  /* strictly ascending bounds        */
+  int32_t splits[ATTN_MAX_SPLIT_BUCKETS];       /* active partitions, >= 1          */
+} attn_split_policy;
+
 /* ---------------------------------------------------------------------------
  * attn_cache_write -- write new tokens' K and V into their cache slots.
  * vLLM PR #64064, sections "Claims" and "Details": V is read with ITS OWN head
@@ -153,6 +171,7 @@ size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t h
  *   softmax_scale  multiplies q.k (fp32), e.g. 1/sqrt(head_dim_k).
  *   num_partitions P >= 1: each sequence's keys are cut into P ranges of
  *            ceil(seq_len/P) keys (rounded up to the kernel's 16-key tile).
+ *   policy   NULL, or the split policy above (then P is the launch's maximum).
  *   workspace      >= attn_splitkv_workspace_bytes(num_seqs, num_q_heads,
  *            head_dim_v, P) bytes of device memory, 256-byte aligned.
  *   out      [num_seqs, num_q_heads, head_dim_v] bf16 contiguous.  If out is
@@ -164,7 +183,7 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
                                 int32_t num_seqs, int32_t num_q_heads,
                                 const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                                 const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
-                                void* workspace, size_t workspace_bytes,
+                                const attn_split_policy* policy, void* workspace, size_t workspace_bytes,
                                 void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -190,7 +209,7 @@ attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int6
                                        int32_t num_seqs, int32_t num_q_heads,
                                        const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                                        const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
-                                       const void* key, int64_t key_stride_tok, int64_t key_stride_head,
+                                       const attn_split_policy* policy, const void* key, int64_t key_stride_tok, int64_t key_stride_head,
                                        const void* value, int64_t val_stride_tok, int64_t val_stride_head,
                                        const int64_t* slot_mapping,
                                        void* workspace, size_t workspace_bytes,
@@ -250,7 +269,7 @@ attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_he
                         int32_t max_query_len, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
                         const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
-                        void* workspace, size_t workspace_bytes,
+                        const attn_split_policy* policy, void* workspace, size_t workspace_bytes,
                         void* out, float* out_lse, const float* sinks, void* stream);
 
 /* Thread-local description of the last non-OK status returned on this thread. */

@@ -214,9 +214,26 @@ def partition_ranges(seq_len: int, num_partitions: int, block_size: int):
     return [(min(p * chunk, seq_len), min((p + 1) * chunk, seq_len)) for p in range(num_partitions)]
 
 
+def active_splits(seq_len: int, num_partitions: int, policy=None) -> int:
+    """A sequence's active split count under a context-bucket policy (vLLM PR #50371, review
+    thread: the split count chosen per runtime sequence length by context buckets, one table
+    for both stages): policy = [(max_seq_len, splits), ...] ascending; the first bucket whose
+    bound holds seq_len decides (the last one for longer sequences), capped at num_partitions."""
+    if not policy:
+        return num_partitions
+    k = policy[-1][1]
+    for bound, splits in policy:
+        if seq_len <= bound:
+            k = splits
+            break
+    return max(1, min(k, num_partitions))
+
+
 def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, cache_flat, spec, scale,
-                             num_partitions, k_scale=None, v_scale=None):
-    """Per-partition normalised outputs [T, Hq, P, Dv] and lse [T, Hq, P] (empty -> 0, -inf)."""
+                             num_partitions, k_scale=None, v_scale=None, policy=None):
+    """Per-partition normalised outputs [T, Hq, P, Dv] and lse [T, Hq, P] (empty -> 0, -inf).
+    With a policy, a sequence splits its keys over its first active_splits(...) partitions
+    only; the rest stay empty."""
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     q = bf16_to_f64(np.asarray(q_bits).view(np.uint16))
     T, Hq = q.shape[0], q.shape[1]
@@ -228,7 +245,7 @@ def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, ca
         S, L = int(seq_lens[b]), t1 - t0
         K, V = gather_kv(cache_flat, spec, block_tables[b], S, k_scale, v_scale)
         pos = S - L + np.arange(L)
-        for p, rng in enumerate(partition_ranges(S, P, spec.block_size)):
+        for p, rng in enumerate(partition_ranges(S, active_splits(S, P, policy), spec.block_size)):
             if rng[1] <= rng[0]:
                 continue
             o, l = attention_rows(q[t0:t1], K, V, pos, scale, key_range=rng)

@@ -89,6 +89,27 @@ size_t splitkv_bytes(int64_t rows, int64_t hq, int64_t dv, int64_t P) {
   return align256(part) + align256(lse);
 }
 
+// The caller's split policy -> the kernels' copy (ok == false: invalid table).
+bool make_policy(const attn_split_policy* p, pa::SplitPolicy* out, const char* who, attn_status* st) {
+  *out = pa::SplitPolicy{};
+  if (!p) return true;
+  if (p->num_buckets < 0 || p->num_buckets > ATTN_MAX_SPLIT_BUCKETS) {
+    *st = fail(ATTN_E_INVALID, "%s: split policy with %d buckets (0..%d)", who, p->num_buckets, ATTN_MAX_SPLIT_BUCKETS);
+    return false;
+  }
+  out->n = p->num_buckets;
+  for (int i = 0; i < p->num_buckets; ++i) {
+    if (p->splits[i] < 1 || (i > 0 && p->max_seq_len[i] <= p->max_seq_len[i - 1])) {
+      *st = fail(ATTN_E_INVALID, "%s: split policy bucket %d: splits must be >= 1 and bounds strictly ascending",
+                 who, i);
+      return false;
+    }
+    out->max_len[i] = p->max_seq_len[i];
+    out->splits[i] = p->splits[i];
+  }
+  return true;
+}
+
 // New tokens' K/V to write before a decode (attn_decode_splitkv_append).
 struct Append {
   const void* key; int64_t k_st, k_sh;
@@ -99,8 +120,8 @@ struct Append {
 attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_sh, const int32_t* qsl,
                         int32_t num_seqs, int32_t rows, int32_t max_q, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* bt, int32_t bt_stride, const int32_t* seq_lens,
-                        float scale, int32_t P, void* ws, size_t ws_bytes, void* out, float* out_lse,
-                        const float* sinks, void* stream, const Append* app = nullptr) {
+                        float scale, int32_t P, const attn_split_policy* policy, void* ws, size_t ws_bytes,
+                        void* out, float* out_lse, const float* sinks, void* stream, const Append* app = nullptr) {
   pa::CacheView c;
   attn_status st = make_view(cache, &c, who);
   if (st != ATTN_OK) return st;
@@ -137,6 +158,7 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   a.seq_lens = seq_lens;
   a.scale = scale;
   a.num_partitions = P;
+  if (!make_policy(policy, &a.pol, who, &st)) return st;
   a.part_out = static_cast<float*>(ws);
   const size_t part_bytes = align256((size_t)rows * num_q_heads * P * c.dv * sizeof(float));
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes);
@@ -167,7 +189,9 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   pa::launch_splitkv_partial(a, s);
   st = check_launch(who);
   if (st != ATTN_OK || !out) return st;
-  pa::MergeArgs m{a.part_out, a.part_lse, rows, num_q_heads, c.dv, P, static_cast<uint16_t*>(out), out_lse, sinks};
+  // decode rows are sequences: the merge reads only each row's active partitions
+  pa::MergeArgs m{a.part_out, a.part_lse, rows, num_q_heads, c.dv, P, static_cast<uint16_t*>(out), out_lse, sinks,
+                  qsl ? nullptr : seq_lens, a.pol};
   pa::launch_merge(m, s);
   return check_launch(who);
 }
@@ -214,36 +238,38 @@ size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t h
 attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_stride_head, int32_t num_seqs,
                                 int32_t num_q_heads, const attn_cache_desc* cache, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, float softmax_scale,
-                                int32_t num_partitions, void* workspace, size_t workspace_bytes, void* out,
-                                float* out_lse, const float* sinks, void* stream) {
+                                int32_t num_partitions, const attn_split_policy* policy, void* workspace,
+                                size_t workspace_bytes, void* out, float* out_lse, const float* sinks, void* stream) {
   return run_splitkv("attn_decode_splitkv", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
-                     num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
-                     workspace_bytes, out, out_lse, sinks, stream);
+                     num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, policy,
+                     workspace, workspace_bytes, out, out_lse, sinks, stream);
 }
 
 attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                                        int32_t num_seqs, int32_t num_q_heads, const attn_cache_desc* cache,
                                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
-                                       float softmax_scale, int32_t num_partitions, const void* key,
+                                       float softmax_scale, int32_t num_partitions, const attn_split_policy* policy,
+                                       const void* key,
                                        int64_t key_stride_tok, int64_t key_stride_head, const void* value,
                                        int64_t val_stride_tok, int64_t val_stride_head, const int64_t* slot_mapping,
                                        void* workspace, size_t workspace_bytes, void* out, float* out_lse,
                                        const float* sinks, void* stream) {
   const Append app{key, key_stride_tok, key_stride_head, value, val_stride_tok, val_stride_head, slot_mapping};
   return run_splitkv("attn_decode_splitkv_append", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
-                     num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, workspace,
-                     workspace_bytes, out, out_lse, sinks, stream, &app);
+                     num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, policy,
+                     workspace, workspace_bytes, out, out_lse, sinks, stream, &app);
 }
 
 attn_status attn_verify(const void* q, int64_t q_stride_tok, int64_t q_stride_head, const int32_t* query_start_loc,
                         int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
                         const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
-                        const int32_t* seq_lens, float softmax_scale, int32_t num_partitions, void* workspace,
-                        size_t workspace_bytes, void* out, float* out_lse, const float* sinks, void* stream) {
+                        const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
+                        const attn_split_policy* policy, void* workspace, size_t workspace_bytes, void* out,
+                        float* out_lse, const float* sinks, void* stream) {
   if (num_seqs > 0 && !query_start_loc) return fail(ATTN_E_INVALID, "attn_verify: NULL query_start_loc");
   return run_splitkv("attn_verify", q, q_stride_tok, q_stride_head, query_start_loc, num_seqs, num_tokens,
                      max_query_len, num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale,
-                     num_partitions, workspace, workspace_bytes, out, out_lse, sinks, stream);
+                     num_partitions, policy, workspace, workspace_bytes, out, out_lse, sinks, stream);
 }
 
 attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t rows, int32_t num_q_heads,
@@ -258,7 +284,7 @@ attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t
     return fail(ATTN_E_UNSUPPORTED, "%s: %d partitions exceed the merge kernel's limit of 4096", who, num_partitions);
   if (head_dim_v % 4) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim_v must be a multiple of 4", who);
   pa::MergeArgs m{part_out, part_lse, rows, num_q_heads, head_dim_v, num_partitions, static_cast<uint16_t*>(out),
-                  out_lse, sinks};
+                  out_lse, sinks, nullptr, pa::SplitPolicy{}};
   pa::launch_merge(m, static_cast<hipStream_t>(stream));
   return check_launch(who);
 }

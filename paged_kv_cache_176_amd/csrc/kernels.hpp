@@ -28,6 +28,23 @@ struct CacheWriteArgs {
 // Returns false if no kernel instance matches (caller reports UNSUPPORTED).
 bool launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 
+// Device-side split policy (context buckets -> active partitions), one table read by
+// every partial kernel and by the merge: a sequence of seq_len S uses the first
+// active_splits(pol, S, P) of the launch's P partitions, the others come out empty.
+constexpr int kMaxSplitBuckets = 8;
+struct SplitPolicy {
+  int32_t n;                            // buckets in use; 0: all P partitions active
+  int32_t max_len[kMaxSplitBuckets];    // ascending upper bounds (inclusive)
+  int32_t splits[kMaxSplitBuckets];
+};
+__host__ __device__ inline int active_splits(const SplitPolicy& pol, int S, int P) {
+  if (pol.n <= 0) return P;
+  int k = pol.splits[pol.n - 1];
+  for (int i = pol.n - 1; i >= 0; --i)
+    if (S <= pol.max_len[i]) k = pol.splits[i];   // ends on the first bucket holding S
+  return k < 1 ? 1 : (k > P ? P : k);
+}
+
 struct SplitArgs {
   const uint16_t* q; int64_t q_st, q_sh;
   const int32_t* qsl;       // null: row b is sequence b with one query
@@ -37,6 +54,7 @@ struct SplitArgs {
   const int32_t* seq_lens;
   float scale;
   int32_t num_partitions;
+  SplitPolicy pol;
   float* part_out; float* part_lse;
   int32_t rows;             // total query rows (tokens)
   // decode only: token b's new K/V row, written into slot aslot[b] (-1: none) by the
@@ -71,6 +89,10 @@ struct MergeArgs {
   int32_t rows, num_q_heads, dv, num_partitions;
   uint16_t* out; float* out_lse;
   const float* sinks;       // [num_q_heads] extra denominator logits, or null
+  // rows that are sequences (decode): row r reads only the first
+  // active_splits(pol, seq_lens[r], P) partials (the rest are empty); null: all P
+  const int32_t* seq_lens;
+  SplitPolicy pol;
 };
 bool launch_merge(const MergeArgs& a, hipStream_t s);
 

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
   const int S = a.seq_lens[b];
   const int q0 = a.qsl ? a.qsl[b] : b;
   const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
-  const int chunk = ceil_div(ceil_div(S, P), 16) * 16;
+  const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, 16);
@@ -378,6 +378,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   __shared__ f32x4 gs[NG][SLOTS];
   const int64_t rh = blockIdx.x;                     // row * Hq + head
   const int P = a.num_partitions, DV = a.dv;
+  // partitions past the row's active count are empty: not read
+  const int Pa = a.seq_lens ? active_splits(a.pol, a.seq_lens[rh / a.num_q_heads], P) : P;
   const int slot = threadIdx.x % SLOTS, grp = threadIdx.x / SLOTS;
   const int c4 = blockIdx.y * SLOTS + slot;          // float4 column
   const bool col_ok = c4 * 4 < DV;
@@ -389,11 +391,11 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int p = grp + k * NG;
-    pre[k] = (col_ok && p < P) ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    pre[k] = (col_ok && p < Pa) ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float* lse = a.part_lse + rh * P;
   float mx = kNegInf;
-  for (int p = threadIdx.x; p < P; p += NT) mx = fmaxf(mx, lse[p]);
+  for (int p = threadIdx.x; p < Pa; p += NT) mx = fmaxf(mx, lse[p]);
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
   M = fmaxf(M, sk);
   __syncthreads();
   float sum = 0.f;
-  for (int p = threadIdx.x; p < P; p += NT) {
+  for (int p = threadIdx.x; p < Pa; p += NT) {
     const float w = (M == kNegInf) ? 0.f : fast_exp2((lse[p] - M) * kLog2e);
     wsh[p] = w;
     sum += w;
@@ -419,10 +421,10 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int p = grp + k * NG;
-    if (p < P) acc += pre[k] * wsh[p];
+    if (p < Pa) acc += pre[k] * wsh[p];
   }
   if (col_ok)
-    for (int p = grp + PRE * NG; p < P; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
+    for (int p = grp + PRE * NG; p < Pa; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
   gs[grp][slot] = acc;
   __syncthreads();
   if (threadIdx.x < SLOTS && c4 * 4 < DV) {
@@ -449,12 +451,14 @@ __global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
   const int c4 = (int)(idx - rh * c4n);
   const float* lse = a.part_lse + rh * P;
   const float* po = a.part_out + rh * P * DV + c4 * 4;
+  // partitions past the row's active count are empty: not read
+  const int Pa = a.seq_lens ? active_splits(a.pol, a.seq_lens[rh / a.num_q_heads], P) : P;
   float lp[PMAX];
   f32x4 op[PMAX];
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
-    lp[p] = p < P ? lse[p] : kNegInf;
-    op[p] = p < P ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    lp[p] = p < Pa ? lse[p] : kNegInf;
+    op[p] = p < Pa ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float M = kNegInf;
 #pragma unroll
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
   if (M != kNegInf) {
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-      const float w = p < P ? fast_exp2((lp[p] - M) * kLog2e) : 0.f;
+      const float w = p < Pa ? fast_exp2((lp[p] - M) * kLog2e) : 0.f;
       tot += w;
       acc += op[p] * w;
     }

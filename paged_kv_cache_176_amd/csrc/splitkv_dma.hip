@@ -74,7 +74,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int S = a.seq_lens[b];
   const int q0 = a.qsl ? a.qsl[b] : b;
   const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
-  const int chunk = ceil_div(ceil_div(S, P), TT) * TT;
+  const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), TT) * TT;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, TT);

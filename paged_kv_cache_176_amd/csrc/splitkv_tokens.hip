@@ -75,7 +75,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
   const int Lq = min(L, a.max_q);
   if (tg * NTOK >= Lq) return;                     // no token of this sequence here (uniform)
-  const int chunk = ceil_div(ceil_div(S, P), 16) * 16;
+  const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, TT);

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int S = a.seq_lens[b];
   const int q0 = a.qsl ? a.qsl[b] : b;
   const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
-  const int chunk = ceil_div(ceil_div(S, P), 16) * 16;
+  const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, TT);

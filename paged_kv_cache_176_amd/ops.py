@@ -66,13 +66,14 @@ def load_library(path: Optional[str] = None):
     lib.attn_cache_write.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, dp, vp]
     lib.attn_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_splitkv_workspace_bytes.restype = sz
-    lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp, vp]
-    lib.attn_decode_splitkv_append.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32,
+    pp = ctypes.POINTER(_SplitPolicyC)
+    lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, sz, vp, vp, vp, vp]
+    lib.attn_decode_splitkv_append.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, pp,
                                                vp, i64, i64, vp, i64, i64, vp, vp, sz, vp, vp, vp, vp]
     lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp, vp]
-    lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, vp, sz, vp, vp, vp,
-                                vp]
+    lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, sz, vp, vp,
+                                vp, vp]
     for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append", "attn_merge_lse",
                  "attn_prefill_causal", "attn_verify"):
         getattr(lib, name).restype = ctypes.c_int
@@ -191,6 +192,27 @@ def workspace_views(ws: torch.Tensor, rows, num_q_heads, head_dim_v, P):
     return po, pl
 
 
+MAX_SPLIT_BUCKETS = 8
+
+
+class _SplitPolicyC(ctypes.Structure):
+    _fields_ = [("num_buckets", ctypes.c_int32), ("max_seq_len", ctypes.c_int32 * MAX_SPLIT_BUCKETS),
+                ("splits", ctypes.c_int32 * MAX_SPLIT_BUCKETS)]
+
+
+def _policy(split_policy):
+    """[(max_seq_len, splits), ...] ascending (the last bucket also takes longer sequences) -> C table."""
+    if split_policy is None:
+        return None
+    if not 0 < len(split_policy) <= MAX_SPLIT_BUCKETS:
+        raise ValueError(f"a split policy has 1..{MAX_SPLIT_BUCKETS} buckets")
+    c = _SplitPolicyC()
+    c.num_buckets = len(split_policy)
+    for i, (bound, k) in enumerate(split_policy):
+        c.max_seq_len[i], c.splits[i] = int(bound), int(k)
+    return ctypes.byref(c)
+
+
 def _sinks(sinks: Optional[torch.Tensor], num_q_heads: int):
     """Device fp32 [num_q_heads] sink logits (or None) -> pointer."""
     if sinks is None:
@@ -212,9 +234,11 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
                    softmax_scale: float, num_partitions: int, out: Optional[torch.Tensor] = None,
                    out_lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                    partials_only: bool = False, with_lse: bool = True, sinks: Optional[torch.Tensor] = None,
-                   stream=None):
+                   split_policy=None, stream=None):
     """One query per sequence: q [B, Hq, Dk] bf16 -> (out [B, Hq, Dv] bf16, lse [B, Hq] fp32, workspace).
-    sinks: optional [Hq] fp32 logits joining each row's softmax denominator (applied by the merge)."""
+    sinks: optional [Hq] fp32 logits joining each row's softmax denominator (applied by the merge).
+    split_policy: optional [(max_seq_len, splits), ...] context buckets choosing each sequence's active
+    partitions on the device (num_partitions is then the launch's maximum)."""
     load_library()
     _need(q, torch.bfloat16, "q")
     _need(block_tables, torch.int32, "block_tables")
@@ -228,7 +252,8 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
     d = cache.c_struct()
     _check(_lib.attn_decode_splitkv(
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
-        _ptr(seq_lens), float(softmax_scale), num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy), _ptr(ws),
+        ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
         _stream(stream)))
     return out, out_lse, ws
@@ -239,7 +264,8 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
                           seq_lens: torch.Tensor, softmax_scale: float, num_partitions: int,
                           out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, partials_only: bool = False,
-                          with_lse: bool = True, sinks: Optional[torch.Tensor] = None, stream=None):
+                          with_lse: bool = True, sinks: Optional[torch.Tensor] = None, split_policy=None,
+                          stream=None):
     """cache_write(key [B, Hkv, Dk], value [B, Hkv, Dv] or None, slot_mapping [B]) followed by
     decode_splitkv, as one call (the write rides in the decode kernel where it can)."""
     load_library()
@@ -263,7 +289,7 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
     d = cache.c_struct()
     _check(_lib.attn_decode_splitkv_append(
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
-        _ptr(seq_lens), float(softmax_scale), num_partitions,
+        _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy),
         _ptr(key), key.stride(0), key.stride(1),
         _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
         _ptr(slot_mapping), _ptr(ws), ws.numel() * ws.element_size(),
@@ -314,7 +340,7 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
            cache: CacheDesc, softmax_scale: float, max_query_len: int, num_partitions: int,
            out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, partials_only: bool = False, with_lse: bool = True,
-           sinks: Optional[torch.Tensor] = None, stream=None):
+           sinks: Optional[torch.Tensor] = None, split_policy=None, stream=None):
     load_library()
     _need(q, torch.bfloat16, "q")
     T, Hq = q.shape[0], q.shape[1]
@@ -327,7 +353,7 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
     _check(_lib.attn_verify(
         _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
         ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
-        num_partitions, _ptr(ws), ws.numel() * ws.element_size(),
+        num_partitions, _policy(split_policy), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
         _stream(stream)))
     return out, out_lse, ws

@@ -85,9 +85,9 @@ def test_splitkv_argument_checks(lib):
     ws_need = lib.attn_splitkv_workspace_bytes(2, 8, 128, 4)
     assert ws_need >= 2 * 8 * 4 * 129 * 4
     assert lib.attn_splitkv_workspace_bytes(-1, 8, 128, 4) == 0
-    args = lambda P, ws_bytes, hq=8: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, hq, ctypes.byref(d),
-                                      ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
-                                      ctypes.c_void_p(0x40000), ws_bytes, ctypes.c_void_p(0x50000), None, None,
+    args = lambda P, ws_bytes, hq=8, pol=None: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, hq, ctypes.byref(d),
+                                                ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P, pol,
+                                                ctypes.c_void_p(0x40000), ws_bytes, ctypes.c_void_p(0x50000), None, None,
                                       None)
     assert lib.attn_decode_splitkv(*args(0, ws_need)) == ops.ATTN_E_INVALID
     assert lib.attn_decode_splitkv(*args(5000, ws_need)) == ops.ATTN_E_INVALID
@@ -100,6 +100,16 @@ def test_splitkv_argument_checks(lib):
     a = list(args(4, ws_need))
     a[5] = ctypes.byref(d2)
     assert lib.attn_decode_splitkv(*a) == ops.ATTN_E_UNSUPPORTED
+    # split policies: bucket count, ascending bounds and splits >= 1 are checked on the host
+    bad = ops._SplitPolicyC()
+    bad.num_buckets = 9
+    assert lib.attn_decode_splitkv(*args(4, ws_need, pol=ctypes.byref(bad))) == ops.ATTN_E_INVALID
+    bad.num_buckets = 2
+    bad.max_seq_len[0], bad.max_seq_len[1], bad.splits[0], bad.splits[1] = 4096, 4096, 8, 16
+    assert lib.attn_decode_splitkv(*args(4, ws_need, pol=ctypes.byref(bad))) == ops.ATTN_E_INVALID
+    assert "ascending" in lib.attn_last_error().decode()
+    bad.max_seq_len[1], bad.splits[1] = 65536, 0
+    assert lib.attn_decode_splitkv(*args(4, ws_need, pol=ctypes.byref(bad))) == ops.ATTN_E_INVALID
 
 
 def test_append_decode_argument_checks(lib):
@@ -109,7 +119,7 @@ def test_append_decode_argument_checks(lib):
     ws_need = lib.attn_splitkv_workspace_bytes(2, 8, 128, 4)
     key, slots = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000)
     args = lambda key, slots, P=4, ks=768: (ctypes.c_void_p(0x10000), 8 * 192, 192, 2, 8, ctypes.byref(d),
-                                            ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P,
+                                            ctypes.c_void_p(0x20000), 8, ctypes.c_void_p(0x30000), 0.07, P, None,
                                             key, ks, 192, ctypes.c_void_p(0x80000), 512, 128, slots,
                                             ctypes.c_void_p(0x40000), ws_need, ctypes.c_void_p(0x50000), None, None,
                                             None)
