@@ -189,9 +189,10 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   pa::launch_splitkv_partial(a, s);
   st = check_launch(who);
   if (st != ATTN_OK || !out) return st;
-  // decode rows are sequences: the merge reads only each row's active partitions
+  // under a split policy, decode rows (rows are sequences) merge only their active partitions;
+  // without one the merge never reads seq_lens
   pa::MergeArgs m{a.part_out, a.part_lse, rows, num_q_heads, c.dv, P, static_cast<uint16_t*>(out), out_lse, sinks,
-                  qsl ? nullptr : seq_lens, a.pol};
+                  (qsl || a.pol.n == 0) ? nullptr : seq_lens, a.pol};
   pa::launch_merge(m, s);
   return check_launch(who);
 }
