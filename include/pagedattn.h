@@ -259,7 +259,9 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
  * scales applied after the dot products (Q stays bf16: fp8 QK^T was rejected,
  * "Benchmarks").  Padded rows (seq_len 0) output exact zeros ("Update
  * 2026-10-01").  Arguments as attn_prefill_causal, plus the split-KV
- * num_partitions and workspace as attn_decode_splitkv (rows = num_tokens).
+ * num_partitions, policy and workspace as attn_decode_splitkv (rows =
+ * num_tokens; the merge of verify rows reads all num_partitions partials, the
+ * inactive ones being empty).
  * DiffKV rows: max_query_len * (num_q_heads/num_kv_heads) must be <= 64.  The
  * bf16 MLA latent row: any max_query_len with <= 16 query heads per KV head
  * (vLLM PR #50371, review thread: the verify that the single-token MLA path
