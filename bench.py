@@ -60,13 +60,17 @@ def _copies(nbytes):
 CUS = 256
 
 
-def auto_partitions(batch, kv_heads, ctx, wgs_per_cu=1, min_keys=256):
+def auto_partitions(batch, kv_heads, ctx, wgs_per_cu=1, min_keys=256, wave_keys=64):
     """Split count: as many 4-wave workgroups as the partial kernel keeps resident per CU
     (two for the bf16 DiffKV decode kernel, one for the MLA and fp8-verify kernels), with
-    partitions of at least min_keys keys."""
+    partitions of at least min_keys keys, then the partition size rounded up to a multiple
+    of wave_keys (one 16-key tile per wave of the workgroup) so that the waves of a
+    workgroup get equal tile counts (100K-key MLA at batch 1: 224 partitions of 448 keys
+    instead of 256 of 400, whose waves got 7 or 6 tiles)."""
     p = max(1, math.ceil(CUS * wgs_per_cu / max(1, batch * kv_heads)))
     p = min(p, max(1, ctx // min_keys), 4096)
-    return p
+    chunk = math.ceil(math.ceil(ctx / p) / wave_keys) * wave_keys
+    return max(1, math.ceil(ctx / chunk))
 
 
 class DecodeCase:

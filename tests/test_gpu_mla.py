@@ -57,7 +57,7 @@ def test_peaked_mla(gpu_lib):
 
 
 # the first split of each batch is the one bench.py times
-@pytest.mark.parametrize("B,Ps", [(1, (256, 96)), (16, (16, 32))])
+@pytest.mark.parametrize("B,Ps", [(1, (224, 256, 96)), (16, (16, 32))])
 def test_mla_config(gpu_lib, B, Ps):
     log(f"MLA config B={B}: generating")
     w = workloads.mla_decode(B, 100000)

@@ -76,7 +76,7 @@ def test_mla_verify_peaked(gpu_lib):
 
 
 # the split count is the one bench.py times
-@pytest.mark.parametrize("B,P", [(1, 256), (4, 64)])
+@pytest.mark.parametrize("B,P", [(1, 224), (4, 64)])
 def test_mla_verify_config(gpu_lib, B, P):
     log(f"MLA verify B={B} x 100000, 4 tokens: generating")
     w = workloads.mla_verify(B, 100000, qlen=4)
