@@ -103,3 +103,14 @@ def test_mla_above_4gb(gpu_lib):
     o1, l1, _ = pk.decode_splitkv(small.q, small.desc, small.bt, small.seq_lens, w.softmax_scale, 9)
     o2, l2, _ = pk.decode_splitkv(small.q, big.desc, big.bt, small.seq_lens, w.softmax_scale, 9)
     assert torch.equal(o1, o2) and torch.equal(l1, l2), "MLA decode differs above 4 GB"
+    # the multi-token MLA verify (shared-ring token kernel)
+    w = workloads.paged_workload("bigmv", workloads.mla_geom(0, 16), [1500, 70], [4, 3], 12, 1 / math.sqrt(576),
+                                 seed=85, std=0.1)
+    small = Uploaded(w)
+    small.write()
+    big = Lifted(small, 240_000)
+    o1, l1, _ = pk.verify(small.q, small.qsl, small.seq_lens, small.bt, small.desc, w.softmax_scale, 4, 7)
+    o2, l2, _ = pk.verify(small.q, small.qsl, small.seq_lens, big.bt, big.desc, w.softmax_scale, 4, 7)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "MLA verify differs above 4 GB"
+    ref, ref_lse = oracle_attention(w, small.cache_bytes())
+    compare(o1, ref, lse_gpu=l1, lse_ref=ref_lse, what="compact MLA verify")
