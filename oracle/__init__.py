@@ -8,8 +8,10 @@ thing both sides consume is the seeded input generators in ``workloads``.
 Contents
   * ``e4m3fn``   -- OCP E4M3FN decode (closed form) and the saturating RNE
                     quantiser used by the fp8 cache write.
-  * ``paged_ref`` -- cache write, paged gather, exact softmax attention with
-                    GQA and causal offsets, split-KV partials and the
+  * ``paged_ref`` -- cache write (any cache strides: NHD, HND, padded pitches),
+                    paged gather, exact softmax attention with GQA, causal
+                    offsets and optional sink logits, split-KV partials under a
+                    fixed count or a context-bucket split policy, and the
                     log-sum-exp merge.
 
 Every function is pinned by ``-m "not gpu"`` tests (closed forms, invariants,
