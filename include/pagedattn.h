@@ -18,6 +18,9 @@
  *     kernels on `stream` (a hipStream_t; NULL = the default stream).  The caller
  *     keeps the buffers alive until that work completes.
  *   - Strides are in ELEMENTS of the tensor they describe.
+ *   - Alignment (else ATTN_E_UNSUPPORTED): q and the cache base, strides and
+ *     v_offset 16 bytes; bf16 outputs `out` 8 bytes; fp32 arrays (lse, sinks)
+ *     4 bytes; split-KV workspaces 256 bytes (ATTN_E_INVALID).
  *   - Status: ATTN_OK, or ATTN_E_INVALID for bad host-side arguments (null
  *     pointers, negative sizes, inconsistent geometry, a workspace that is too
  *     small), ATTN_E_UNSUPPORTED when no kernel exists for a shape or dtype
@@ -68,7 +71,12 @@ typedef enum { ATTN_SCALE_NONE = 0, ATTN_SCALE_PER_TENSOR = 1, ATTN_SCALE_PER_HE
  * slot j % block_size.  K occupies columns [0, head_dim_k), V occupies
  * [v_offset, v_offset + head_dim_v); both must fit in row_dim.  The default
  * (NHD) strides are stride_head = row_dim, stride_slot = num_kv_heads*row_dim,
- * stride_block = block_size*stride_slot.
+ * stride_block = block_size*stride_slot; HND swaps the slot and head strides
+ * (stride_slot = row pitch, stride_head = block_size*row pitch).  Strides must
+ * be positive and must not let two rows share an element: ordered by stride, the
+ * slot and head strides (of dims with more than one index) must each be at
+ * least the extent of what nests inside them, starting from row_dim, and
+ * stride_block at least one block's extent; else ATTN_E_INVALID.
  * DiffKV: row_dim 320, head_dim_k 192, head_dim_v 128, v_offset 192.
  * MLA:    row_dim 576, head_dim_k 576, head_dim_v 512, v_offset 0.          */
 typedef struct {
@@ -139,7 +147,7 @@ attn_status attn_cache_write(const void* key, int64_t key_stride_tok, int64_t ke
  * num_q_heads, num_partitions] fp32 (-inf for an empty range) at the next
  * 256-byte boundary.  Contents need no initialisation.  Two calls that share a
  * workspace must not run concurrently.  Returns the bytes needed (0 for invalid
- * arguments).                                                                  */
+ * arguments, or a size that does not fit in 62 bits).                          */
 size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim_v,
                                     int32_t num_partitions);
 
@@ -222,9 +230,12 @@ attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int6
  * 2026-10-01"); otherwise w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p,
  * lse = M + ln sum w_p.  With sinks, sink_h joins as one more partial with
  * lse = sink_h and a zero output (see "Sink logits").
- *   part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 contiguous;
+ *   part_out [rows, num_q_heads, num_partitions, head_dim_v] fp32 contiguous,
+ *            16-byte aligned;
  *   part_lse [rows, num_q_heads, num_partitions] fp32 contiguous;
- *   out [rows, num_q_heads, head_dim_v] bf16 contiguous; out_lse fp32 or NULL. */
+ *   out [rows, num_q_heads, head_dim_v] bf16 contiguous; out_lse fp32 or NULL.
+ *   head_dim_v must be a multiple of 4 and num_partitions <= 4096, else
+ *   ATTN_E_UNSUPPORTED.                                                        */
 attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t rows, int32_t num_q_heads,
                            int32_t head_dim_v, int32_t num_partitions,
                            void* out, float* out_lse, const float* sinks, void* stream);
@@ -239,7 +250,8 @@ attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t
  *            query_start_loc[b] .. query_start_loc[b+1]-1; L_b is their count.
  *   seq_lens [num_seqs] int32: keys of sequence b INCLUDING this chunk; query i
  *            of b sits at position seq_lens[b] - L_b + i and sees keys 0..that.
- *   max_query_len  >= every L_b (sizes the launch).
+ *   max_query_len  >= every L_b (sizes the launch); 0 with num_tokens > 0 is
+ *            ATTN_E_INVALID.
  *   out [num_tokens, num_q_heads, head_dim_v] bf16 contiguous; out_lse
  *            [num_tokens, num_q_heads] fp32 or NULL.
  *   Rows with no visible key output 0 and lse -inf.                            */

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <utility>
 
 #include "../../include/pagedattn.h"
 #include "kernels.hpp"
@@ -39,8 +40,28 @@ attn_status make_view(const attn_cache_desc* d, pa::CacheView* v, const char* wh
   if (d->head_dim_k > d->row_dim || (int64_t)d->v_offset + d->head_dim_v > d->row_dim)
     return fail(ATTN_E_INVALID, "%s: K [0,%d) or V [%d,%d) does not fit a row of %d", who, d->head_dim_k,
                 d->v_offset, d->v_offset + d->head_dim_v, d->row_dim);
-  if (d->stride_head < d->row_dim || d->stride_slot <= 0 || d->stride_block <= 0)
-    return fail(ATTN_E_INVALID, "%s: non-positive or overlapping cache strides", who);
+  if (d->stride_head <= 0 || d->stride_slot <= 0 || d->stride_block <= 0)
+    return fail(ATTN_E_INVALID, "%s: cache strides must be positive", who);
+  {
+    // No two (block, slot, head) rows may share an element.  Sufficient test: order the
+    // slot and head dims (those with more than one index) by stride; each stride must be
+    // at least the extent of everything nested inside it, and so must the block stride.
+    int64_t st[2], n[2];
+    int k = 0;
+    if (d->block_size > 1) st[k] = d->stride_slot, n[k++] = d->block_size;
+    if (d->num_kv_heads > 1) st[k] = d->stride_head, n[k++] = d->num_kv_heads;
+    if (k == 2 && st[0] > st[1]) std::swap(st[0], st[1]), std::swap(n[0], n[1]);
+    int64_t ext = d->row_dim;
+    for (int i = 0; i < k; ++i) {
+      if (st[i] < ext)
+        return fail(ATTN_E_INVALID, "%s: overlapping cache strides (block %lld, slot %lld, head %lld, row %d)", who,
+                    (long long)d->stride_block, (long long)d->stride_slot, (long long)d->stride_head, d->row_dim);
+      ext += (n[i] - 1) * st[i];
+    }
+    if (d->num_blocks > 1 && d->stride_block < ext)
+      return fail(ATTN_E_INVALID, "%s: overlapping cache strides: block stride %lld < one block's extent %lld", who,
+                  (long long)d->stride_block, (long long)ext);
+  }
   if (d->dtype != ATTN_KV_BF16 && d->dtype != ATTN_KV_FP8_E4M3FN)
     return fail(ATTN_E_INVALID, "%s: unknown cache dtype %d", who, (int)d->dtype);
   if (d->scale_mode < ATTN_SCALE_NONE || d->scale_mode > ATTN_SCALE_PER_HEAD)
@@ -82,11 +103,22 @@ attn_status attention_layout_ok(const pa::CacheView& c, const void* q, int64_t q
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace: part_out | part_lse, each starting on a 256-byte boundary.
+// Workspace: part_out | part_lse, each starting on a 256-byte boundary; 0 when the size
+// does not fit in 62 bits (sizes the library rejects).
 size_t splitkv_bytes(int64_t rows, int64_t hq, int64_t dv, int64_t P) {
-  const size_t part = (size_t)(rows * hq * P * dv) * sizeof(float);
-  const size_t lse = (size_t)(rows * hq * P) * sizeof(float);
+  const unsigned __int128 n = (unsigned __int128)rows * hq * P;
+  if (n * (dv + 1) * sizeof(float) >= ((unsigned __int128)1 << 62)) return 0;
+  const size_t part = (size_t)(n * dv) * sizeof(float);
+  const size_t lse = (size_t)n * sizeof(float);
   return align256(part) + align256(lse);
+}
+
+// Output buffers: bf16 rows are stored 4 elements (8 bytes) at a time, fp32 values singly.
+attn_status outputs_aligned(const void* out, const float* out_lse, const float* sinks, const char* who) {
+  if (!aligned(out, 8)) return fail(ATTN_E_UNSUPPORTED, "%s: out must be 8-byte aligned", who);
+  if (!aligned(out_lse, 4) || !aligned(sinks, 4))
+    return fail(ATTN_E_UNSUPPORTED, "%s: out_lse and sinks must be 4-byte aligned", who);
+  return ATTN_OK;
 }
 
 // The caller's split policy -> the kernels' copy (ok == false: invalid table).
@@ -139,10 +171,14 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
       return fail(ATTN_E_INVALID, "%s: negative key/value strides", who);
   }
   if (bt_stride <= 0) return fail(ATTN_E_INVALID, "%s: bt_stride must be positive", who);
+  if (qsl && max_q == 0) return fail(ATTN_E_INVALID, "%s: %d query tokens but max_query_len 0", who, rows);
   const size_t need = splitkv_bytes(rows, num_q_heads, c.dv, P);
+  if (need == 0) return fail(ATTN_E_INVALID, "%s: workspace size overflows", who);
   if (ws_bytes < need) return fail(ATTN_E_INVALID, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
   if (!aligned(ws, 256)) return fail(ATTN_E_INVALID, "%s: workspace must be 256-byte aligned", who);
   st = attention_layout_ok(c, q, q_st, q_sh, who);
+  if (st != ATTN_OK) return st;
+  st = outputs_aligned(out, out_lse, sinks, who);
   if (st != ATTN_OK) return st;
   pa::SplitArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -284,6 +320,10 @@ attn_status attn_merge_lse(const float* part_out, const float* part_lse, int32_t
   if (num_partitions > 4096)
     return fail(ATTN_E_UNSUPPORTED, "%s: %d partitions exceed the merge kernel's limit of 4096", who, num_partitions);
   if (head_dim_v % 4) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim_v must be a multiple of 4", who);
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4))
+    return fail(ATTN_E_UNSUPPORTED, "%s: part_out must be 16-byte and part_lse 4-byte aligned", who);
+  const attn_status st = outputs_aligned(out, out_lse, sinks, who);
+  if (st != ATTN_OK) return st;
   pa::MergeArgs m{part_out, part_lse, rows, num_q_heads, head_dim_v, num_partitions, static_cast<uint16_t*>(out),
                   out_lse, sinks, nullptr, pa::SplitPolicy{}};
   pa::launch_merge(m, static_cast<hipStream_t>(stream));
@@ -310,6 +350,9 @@ attn_status attn_prefill_causal(const void* q, int64_t q_stride_tok, int64_t q_s
   if (bt_stride <= 0) return fail(ATTN_E_INVALID, "%s: bt_stride must be positive", who);
   st = attention_layout_ok(c, q, q_stride_tok, q_stride_head, who);
   if (st != ATTN_OK) return st;
+  st = outputs_aligned(out, out_lse, sinks, who);
+  if (st != ATTN_OK) return st;
+  if (max_query_len == 0) return fail(ATTN_E_INVALID, "%s: %d query tokens but max_query_len 0", who, num_tokens);
   pa::PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_st = q_stride_tok;

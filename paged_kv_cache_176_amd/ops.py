@@ -105,7 +105,8 @@ class CacheDesc:
 
     Element (block, slot, head, col) is at storage_base + block*stride_block +
     slot*stride_slot + head*stride_head + col, in cache elements (2 bytes for
-    bf16, 1 byte for fp8).
+    bf16, 1 byte for fp8).  The checked C descriptor is built on first use and kept
+    until a field is assigned again.
     """
     storage: torch.Tensor
     num_blocks: int
@@ -123,6 +124,10 @@ class CacheDesc:
     v_scale: Optional[torch.Tensor] = None
     scale_mode: str = "none"
 
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        object.__setattr__(self, "_c", None)            # any change: check and rebuild on next use
+
     def __post_init__(self):
         if self.stride_head is None:
             self.stride_head = self.row_dim
@@ -137,8 +142,37 @@ class CacheDesc:
                    geom.head_dim_v, geom.v_offset, geom.kv_dtype, geom.stride_block, geom.stride_slot,
                    geom.stride_head, k_scale, v_scale, scale_mode)
 
+    def extent_bytes(self) -> int:
+        """Bytes from the storage's first element to the end of the last row the strides address."""
+        esize = 1 if self.kv_dtype == "fp8" else 2
+        last = ((self.num_blocks - 1) * self.stride_block + (self.block_size - 1) * self.stride_slot +
+                (self.num_kv_heads - 1) * self.stride_head + self.row_dim)
+        return last * esize
+
     def c_struct(self) -> _CacheDescC:
+        if self._c is None:
+            object.__setattr__(self, "_c", self._build())
+        return self._c
+
+    def _build(self) -> _CacheDescC:
         mode = {"none": SCALE_NONE, "tensor": SCALE_TENSOR, "head": SCALE_HEAD}[self.scale_mode]
+        if self.storage.device.type != "cuda":
+            raise TypeError("the cache storage must be on the GPU")
+        if self.storage.is_contiguous():              # the storage tensor's own bytes
+            avail = self.storage.numel() * self.storage.element_size()
+        else:                                         # else the allocation past its first element
+            st = self.storage.untyped_storage()
+            avail = st.nbytes() - (self.storage.data_ptr() - st.data_ptr())
+        if self.extent_bytes() > avail:
+            raise ValueError(f"the cache strides address {self.extent_bytes()} bytes but the storage holds {avail}")
+        if self.kv_dtype == "fp8":
+            n = {"tensor": 1, "head": self.num_kv_heads}.get(self.scale_mode)
+            for name, sc in (("k_scale", self.k_scale), ("v_scale", self.v_scale)):
+                if n is None or sc is None:
+                    raise ValueError("an fp8 cache needs k_scale and v_scale, per tensor or per head")
+                _need(sc, torch.float32, name)
+                if sc.numel() != n or not sc.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} values")
         return _CacheDescC(
             self.storage.data_ptr(), self.num_blocks, self.block_size, self.num_kv_heads, self.row_dim,
             self.head_dim_k, self.head_dim_v, self.v_offset, 0, self.stride_block, self.stride_slot,
@@ -154,16 +188,55 @@ def _need(t: torch.Tensor, dtype, name):
         raise TypeError(f"{name} must be on the GPU")
 
 
+def _need_rows(t: Optional[torch.Tensor], dtype, name, shape):
+    """An output or partials buffer: given dtype, on the GPU, contiguous, exactly `shape`."""
+    if t is None:
+        return
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {list(shape)} tensor, got {list(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _need_query(q: torch.Tensor, cache: "CacheDesc", name="q"):
+    """[tokens, Hq, head_dim_k] bf16 with a contiguous last dim (token and head strides are free)."""
+    _need(q, torch.bfloat16, name)
+    if q.dim() != 3 or q.shape[2] != cache.head_dim_k or q.stride(2) != 1:
+        raise ValueError(f"{name} must be [tokens, heads, {cache.head_dim_k}] with a contiguous last dim")
+
+
+def _need_index(t: torch.Tensor, name, numel=None, dtype=torch.int32):
+    _need(t, dtype, name)
+    if t.dim() != 1 or not t.is_contiguous() or (numel is not None and t.numel() != numel):
+        raise ValueError(f"{name} must be a contiguous 1-D {dtype} tensor" +
+                         ("" if numel is None else f" of {numel} entries"))
+
+
+def _need_table(bt: torch.Tensor, num_seqs: int):
+    _need(bt, torch.int32, "block_tables")
+    if bt.dim() != 2 or bt.shape[0] < num_seqs or bt.stride(1) != 1:
+        raise ValueError(f"block_tables must be [>= {num_seqs}, max_blocks] int32 with contiguous rows")
+
+
+def _need_kv(key, value, cache: "CacheDesc", tokens: int):
+    _need(key, torch.bfloat16, "key")
+    if key.dim() != 3 or tuple(key.shape) != (tokens, cache.num_kv_heads, cache.head_dim_k) or key.stride(2) != 1:
+        raise ValueError(f"key must be [{tokens}, {cache.num_kv_heads}, {cache.head_dim_k}] bf16 with a contiguous "
+                         "last dim")
+    if value is not None:
+        _need(value, torch.bfloat16, "value")
+        if (value.dim() != 3 or tuple(value.shape) != (tokens, cache.num_kv_heads, cache.head_dim_v)
+                or value.stride(2) != 1):
+            raise ValueError(f"value must be [{tokens}, {cache.num_kv_heads}, {cache.head_dim_v}] bf16 with a "
+                             "contiguous last dim")
+
+
 def cache_write(key: torch.Tensor, value: Optional[torch.Tensor], slot_mapping: torch.Tensor, cache: CacheDesc,
                 stream=None) -> None:
     """Write key [T, Hkv, Dk] / value [T, Hkv, Dv] (bf16, any token/head strides) into ``cache``."""
     load_library()
-    _need(key, torch.bfloat16, "key")
-    _need(slot_mapping, torch.int64, "slot_mapping")
-    if value is not None:
-        _need(value, torch.bfloat16, "value")
-    if key.stride(-1) != 1 or (value is not None and value.stride(-1) != 1):
-        raise ValueError("the last dim of key/value must be contiguous")
+    _need_kv(key, value, cache, key.shape[0])
+    _need_index(slot_mapping, "slot_mapping", key.shape[0], torch.int64)
     d = cache.c_struct()
     _check(_lib.attn_cache_write(
         _ptr(key), key.stride(0), key.stride(1),
@@ -223,10 +296,20 @@ def _sinks(sinks: Optional[torch.Tensor], num_q_heads: int):
     return _ptr(sinks)
 
 
+def _need_batch(query_start_loc, seq_lens, block_tables):
+    """The per-sequence arrays of a multi-token call (prefill, verify)."""
+    _need_index(seq_lens, "seq_lens")
+    _need_index(query_start_loc, "query_start_loc", seq_lens.numel() + 1)
+    _need_table(block_tables, seq_lens.numel())
+
+
 def _workspace(rows, hq, dv, P, device, ws):
+    """The caller's workspace (checked) or a new one."""
     need = splitkv_workspace_bytes(rows, hq, dv, P)
-    if ws is None or ws.numel() * ws.element_size() < need:
-        ws = new_workspace(rows, hq, dv, P, device)
+    if ws is None:
+        return new_workspace(rows, hq, dv, P, device)
+    if ws.device.type != "cuda" or not ws.is_contiguous() or ws.numel() * ws.element_size() < need:
+        raise ValueError(f"the workspace must be a contiguous GPU buffer of >= {need} bytes")
     return ws
 
 
@@ -240,10 +323,12 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
     split_policy: optional [(max_seq_len, splits), ...] context buckets choosing each sequence's active
     partitions on the device (num_partitions is then the launch's maximum)."""
     load_library()
-    _need(q, torch.bfloat16, "q")
-    _need(block_tables, torch.int32, "block_tables")
-    _need(seq_lens, torch.int32, "seq_lens")
+    _need_query(q, cache)
     B, Hq = q.shape[0], q.shape[1]
+    _need_table(block_tables, B)
+    _need_index(seq_lens, "seq_lens", B)
+    _need_rows(out, torch.bfloat16, "out", (B, Hq, cache.head_dim_v))
+    _need_rows(out_lse, torch.float32, "out_lse", (B, Hq))
     ws = _workspace(B, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
     if not partials_only and out is None:
         out = torch.empty(B, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
@@ -269,18 +354,14 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
     """cache_write(key [B, Hkv, Dk], value [B, Hkv, Dv] or None, slot_mapping [B]) followed by
     decode_splitkv, as one call (the write rides in the decode kernel where it can)."""
     load_library()
-    _need(q, torch.bfloat16, "q")
-    _need(key, torch.bfloat16, "key")
-    _need(slot_mapping, torch.int64, "slot_mapping")
-    if value is not None:
-        _need(value, torch.bfloat16, "value")
-    if key.stride(-1) != 1 or (value is not None and value.stride(-1) != 1):
-        raise ValueError("the last dim of key/value must be contiguous")
-    _need(block_tables, torch.int32, "block_tables")
-    _need(seq_lens, torch.int32, "seq_lens")
+    _need_query(q, cache)
     B, Hq = q.shape[0], q.shape[1]
-    if key.shape[0] != B or slot_mapping.shape[0] != B:
-        raise ValueError("one new token per sequence: key and slot_mapping need num_seqs rows")
+    _need_kv(key, value, cache, B)                  # one new token per sequence
+    _need_index(slot_mapping, "slot_mapping", B, torch.int64)
+    _need_table(block_tables, B)
+    _need_index(seq_lens, "seq_lens", B)
+    _need_rows(out, torch.bfloat16, "out", (B, Hq, cache.head_dim_v))
+    _need_rows(out_lse, torch.float32, "out_lse", (B, Hq))
     ws = _workspace(B, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
     if not partials_only and out is None:
         out = torch.empty(B, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
@@ -308,6 +389,9 @@ def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torc
     if not (part_out.is_contiguous() and part_lse.is_contiguous()):
         raise ValueError("partials must be contiguous")
     rows, Hq, P, Dv = part_out.shape
+    _need_rows(part_lse, torch.float32, "part_lse", (rows, Hq, P))
+    _need_rows(out, torch.bfloat16, "out", (rows, Hq, Dv))
+    _need_rows(out_lse, torch.float32, "out_lse", (rows, Hq))
     if out is None:
         out = torch.empty(rows, Hq, Dv, dtype=torch.bfloat16, device=part_out.device)
     if with_lse and out_lse is None:
@@ -322,8 +406,11 @@ def prefill_causal(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: tor
                    out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
                    with_lse: bool = True, sinks: Optional[torch.Tensor] = None, stream=None):
     load_library()
-    _need(q, torch.bfloat16, "q")
+    _need_query(q, cache)
     T, Hq = q.shape[0], q.shape[1]
+    _need_batch(query_start_loc, seq_lens, block_tables)
+    _need_rows(out, torch.bfloat16, "out", (T, Hq, cache.head_dim_v))
+    _need_rows(out_lse, torch.float32, "out_lse", (T, Hq))
     if out is None:
         out = torch.empty(T, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)
     if with_lse and out_lse is None:
@@ -342,8 +429,11 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
            workspace: Optional[torch.Tensor] = None, partials_only: bool = False, with_lse: bool = True,
            sinks: Optional[torch.Tensor] = None, split_policy=None, stream=None):
     load_library()
-    _need(q, torch.bfloat16, "q")
+    _need_query(q, cache)
     T, Hq = q.shape[0], q.shape[1]
+    _need_batch(query_start_loc, seq_lens, block_tables)
+    _need_rows(out, torch.bfloat16, "out", (T, Hq, cache.head_dim_v))
+    _need_rows(out_lse, torch.float32, "out_lse", (T, Hq))
     ws = _workspace(T, Hq, cache.head_dim_v, num_partitions, q.device, workspace)
     if not partials_only and out is None:
         out = torch.empty(T, Hq, cache.head_dim_v, dtype=torch.bfloat16, device=q.device)

@@ -148,3 +148,39 @@ def test_merge_and_prefill_argument_checks(lib):
 
 def test_version_string(lib):
     assert lib.attn_version().decode().startswith("pagedattn")
+
+
+@pytest.mark.parametrize("bad", [
+    dict(stride_slot=640),                              # NHD slots of 2 heads: slot 1 head 0 == slot 0 head 2
+    dict(stride_head=320, stride_slot=320),             # slot and head dims alias
+    dict(stride_block=15 * 4 * 320),                    # a block one slot too short
+    dict(stride_head=16 * 320, stride_slot=300),        # HND order with a row pitch below row_dim
+])
+def test_overlapping_strides_are_invalid(lib, bad):
+    d = _desc(**bad)
+    st = lib.attn_cache_write(ctypes.c_void_p(0x2000), 768, 192, None, 0, 0, ctypes.c_void_p(0x3000), 3,
+                              ctypes.byref(d), None)
+    assert st == ops.ATTN_E_INVALID
+    assert "overlapping cache strides" in lib.attn_last_error().decode()
+
+
+def test_alignment_and_size_checks(lib):
+    big = 1 << 20
+    # merge: part_out read as float4, out written 4 bf16 at a time
+    assert lib.attn_merge_lse(ctypes.c_void_p(big + 4), ctypes.c_void_p(2 * big), 1, 8, 128, 4,
+                              ctypes.c_void_p(3 * big), None, None, None) == ops.ATTN_E_UNSUPPORTED
+    assert "part_out" in lib.attn_last_error().decode()
+    assert lib.attn_merge_lse(ctypes.c_void_p(big), ctypes.c_void_p(2 * big), 1, 8, 128, 4,
+                              ctypes.c_void_p(3 * big + 2), None, None, None) == ops.ATTN_E_UNSUPPORTED
+    assert "out must be 8-byte aligned" in lib.attn_last_error().decode()
+    # verify: tokens with max_query_len 0, and a misaligned output
+    d = _desc()
+    ws_need = lib.attn_splitkv_workspace_bytes(4, 8, 128, 4)
+    vargs = lambda max_q, out: (ctypes.c_void_p(big), 8 * 192, 192, ctypes.c_void_p(2 * big), 2, 4, max_q, 8,
+                                ctypes.byref(d), ctypes.c_void_p(3 * big), 8, ctypes.c_void_p(4 * big), 0.07, 4, None,
+                                ctypes.c_void_p(5 * big), ws_need, out, None, None, None)
+    assert lib.attn_verify(*vargs(0, ctypes.c_void_p(6 * big))) == ops.ATTN_E_INVALID
+    assert "max_query_len 0" in lib.attn_last_error().decode()
+    assert lib.attn_verify(*vargs(2, ctypes.c_void_p(6 * big + 6))) == ops.ATTN_E_UNSUPPORTED
+    # a workspace size past 62 bits is reported as 0 (invalid), not wrapped
+    assert lib.attn_splitkv_workspace_bytes(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 20, 4096) == 0
