@@ -605,19 +605,25 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     const char* buf = smem + (j % NSTAGE) * STAGE_BYTES;
     f32x16 s0, s1;
     uint32_t p0[8], p1[8];
+    // The two blocks that are MFMAs only (the first half's QK^T, the second half's PV)
+    // run at raised wave priority: while the SIMD's other wave is in a mixed region, the
+    // arbiter issues this wave's MFMAs first and the other wave's softmax fills the
+    // matrix core's gaps (chunked prefill 1.3% faster; the same schedule without the
+    // priority is 2% slower, and raising it over region 1 as well, 2-3% slower).
+    __builtin_amdgcn_s_setprio(1);
     qk_half(buf, 0, s0);
-    // region 1: QK of the second half while the first half's softmax runs.  The block
-    // holds both halves' 24 K-operand reads and 24 MFMAs: reads run three MFMAs ahead
-    // (a read issued just before its MFMA exposes a whole LDS round trip per k-step),
-    // and the first half's softmax fills the gaps between the second half's MFMAs.
+    __builtin_amdgcn_s_setprio(0);
+    // region 1: QK of the second half while the first half's softmax runs: 12 K-operand
+    // reads running three MFMAs ahead (a read issued just before its MFMA exposes a whole
+    // LDS round trip per k-step), the softmax's VALU work between the MFMAs.
     qk_half(buf, 1, s1);
     const float a0 = softmax_half(s0, p0);
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);     // ds_read: operands 0-2
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
+    for (int i = 0; i < KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // mfma i
-      if (i + 3 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // ds_read i + 3
-      if (i >= KS) __builtin_amdgcn_sched_group_barrier(0x402, 5, 1);          // valu / trans
+      if (i + 3 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);       // ds_read i + 3
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 1);   // valu / trans
     }
     if (__any(a0 != 1.0f)) {
 #pragma unroll
@@ -637,6 +643,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= a1;
     }
+    __builtin_amdgcn_s_setprio(1);
     pv_half(buf, 1, p1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);     // ds_read: operands of MFMAs 0-1
 #pragma unroll
@@ -644,6 +651,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);   // mfma i
       if (i + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);   // MFMA i + 2's reads
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Q is complete from here on.  A wait the compiler sees (the ring's waits are inline
