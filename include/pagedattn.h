@@ -128,7 +128,9 @@ typedef struct {
  *          key + t*key_stride_tok + h*key_stride_head + d.
  *   value  [num_tokens, num_kv_heads, head_dim_v] bf16, own strides; may be
  *          NULL, then only the K columns are written (MLA latent rows, whose V
- *          is the row's first head_dim_v columns).
+ *          is the row's first head_dim_v columns).  A value whose columns
+ *          [v_offset, v_offset + head_dim_v) overlap K's [0, head_dim_k) is
+ *          ATTN_E_INVALID (the two writes would race on the shared bytes).
  *   slot_mapping [num_tokens] int64: slot = block*block_size + slot-in-block;
  *          -1 skips the token (padding).
  *   For ATTN_KV_FP8_E4M3FN the stored byte is E4M3FN(fp32(x) / fp32(scale)):
@@ -155,8 +157,8 @@ size_t attn_splitkv_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t h
  * Sink logits (every attention entry point below takes `sinks`): NULL, or a
  * device array [num_q_heads] fp32 of per-query-head logits that join every row's
  * softmax denominator as one extra term with a zero value row (the attention
- * sink read as an extra softmax-denominator logit: diffbot model card, "Known
- * issues" on the vision encoder's sink).  In the units of softmax_scale*q.k:
+ * sink read as an extra softmax-denominator logit: diffbot model card, "Update
+ * 2026-10-01: three correctness fixes", the item on the vision encoder's sink).  In the units of softmax_scale*q.k:
  *   out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h}),
  *   lse = ln(sum_j e^{s_j} + e^{sink_h})   (the denominator actually applied).
  * A row with no visible key then outputs 0 and lse = sink_h.  -inf entries (and

@@ -16,8 +16,8 @@ Plain definitions, written for checking by eye against the pages:
   (review thread: split sweep, runtime split count) and the split-KV reducer of
   the diffbot model card; the merge is the log-sum-exp identity.
 * attention sink: a per-query-head logit that joins the softmax denominator as one
-  more term (diffbot model card, "Known issues": the vision encoder's sink read as an
-  extra softmax-denominator logit).  It is taken here as one more key whose score is
+  more term (diffbot model card, "Update 2026-10-01: three correctness fixes", third
+  item: the vision encoder's sink read as an extra softmax-denominator logit).  It is taken here as one more key whose score is
   the sink and whose value row is zero; lse is the log of the whole denominator.
 
 fp8 caches are dequantised as code value x scale (per tensor or per KV head).
@@ -35,18 +35,6 @@ from . import e4m3fn
 
 def bf16_to_f64(bits) -> np.ndarray:
     return e4m3fn.bf16_bits_to_f32(bits).astype(np.float64)
-
-
-def f64_to_bf16_bits(x) -> np.ndarray:
-    """Round float values to bf16 (nearest, ties to even) via exact integer arithmetic on binary32."""
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lower = u & 0xFFFF
-    upper = u >> 16
-    round_up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
-    out = (upper + round_up.astype(np.uint64)) & 0xFFFF
-    out = np.where(np.isnan(f), 0x7FC0, out)
-    return out.astype(np.uint16)
 
 
 class CacheSpec:
@@ -206,11 +194,18 @@ def paged_attention(q_bits: np.ndarray, query_start_loc, seq_lens, block_tables,
     return out, lse
 
 
-def partition_ranges(seq_len: int, num_partitions: int, block_size: int):
-    """Key ranges of split-KV partitions: chunk = ceil(S / P) rounded up to a multiple of BS."""
+# Split-KV partitions are cut in whole 16-key tiles: the library's documented rule (each
+# of P ranges holds ceil(S / P) keys rounded up to 16), whatever the cache block size.
+PARTITION_TILE = 16
+
+
+def partition_ranges(seq_len: int, num_partitions: int, tile: int = PARTITION_TILE):
+    """Key ranges of split-KV partitions (vLLM PR #50371, review thread: a runtime split count
+    over a sequence's keys): partition p covers [p*C, min((p+1)*C, S)) with C = ceil(S / P)
+    rounded up to a multiple of ``tile``; trailing partitions may be empty."""
     if seq_len == 0:
         return [(0, 0)] * num_partitions
-    chunk = math.ceil(math.ceil(seq_len / num_partitions) / block_size) * block_size
+    chunk = math.ceil(math.ceil(seq_len / num_partitions) / tile) * tile
     return [(min(p * chunk, seq_len), min((p + 1) * chunk, seq_len)) for p in range(num_partitions)]
 
 
@@ -245,7 +240,7 @@ def paged_attention_partials(q_bits, query_start_loc, seq_lens, block_tables, ca
         S, L = int(seq_lens[b]), t1 - t0
         K, V = gather_kv(cache_flat, spec, block_tables[b], S, k_scale, v_scale)
         pos = S - L + np.arange(L)
-        for p, rng in enumerate(partition_ranges(S, active_splits(S, P, policy), spec.block_size)):
+        for p, rng in enumerate(partition_ranges(S, active_splits(S, P, policy))):
             if rng[1] <= rng[0]:
                 continue
             o, l = attention_rows(q[t0:t1], K, V, pos, scale, key_range=rng)

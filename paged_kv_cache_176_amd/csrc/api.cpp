@@ -90,6 +90,15 @@ attn_status make_view(const attn_cache_desc* d, pa::CacheView* v, const char* wh
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// A written value must not share columns with the written key: two threads would store the
+// same bytes in no fixed order (the MLA latent row, V = K's first columns, takes value NULL).
+attn_status value_columns_ok(const pa::CacheView& c, const void* value, const char* who) {
+  if (value && c.v_off < c.dk)   // [v_off, v_off+dv) meets [0, dk): v_off >= 0 and dv > 0
+    return fail(ATTN_E_INVALID, "%s: V columns [%d,%d) overlap K columns [0,%d): pass value NULL when V is part of K",
+                who, c.v_off, c.v_off + c.dv, c.dk);
+  return ATTN_OK;
+}
+
 // Layout requirements of the attention kernels (16-byte row loads).
 attn_status attention_layout_ok(const pa::CacheView& c, const void* q, int64_t q_st, int64_t q_sh, const char* who) {
   const int eb = c.esize;
@@ -169,6 +178,8 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
     if (!app->key || !app->slots) return fail(ATTN_E_INVALID, "%s: NULL key or slot_mapping", who);
     if (app->k_st < 0 || app->k_sh < 0 || app->v_st < 0 || app->v_sh < 0)
       return fail(ATTN_E_INVALID, "%s: negative key/value strides", who);
+    st = value_columns_ok(c, app->value, who);
+    if (st != ATTN_OK) return st;
   }
   if (bt_stride <= 0) return fail(ATTN_E_INVALID, "%s: bt_stride must be positive", who);
   if (qsl && max_q == 0) return fail(ATTN_E_INVALID, "%s: %d query tokens but max_query_len 0", who, rows);
@@ -253,6 +264,8 @@ attn_status attn_cache_write(const void* key, int64_t key_stride_tok, int64_t ke
   if (!key || !slot_mapping) return fail(ATTN_E_INVALID, "%s: NULL key or slot_mapping", who);
   if (key_stride_tok < 0 || key_stride_head < 0 || val_stride_tok < 0 || val_stride_head < 0)
     return fail(ATTN_E_INVALID, "%s: negative source strides", who);
+  st = value_columns_ok(c, value, who);
+  if (st != ATTN_OK) return st;
   pa::CacheWriteArgs a;
   a.key = static_cast<const uint16_t*>(key);
   a.k_st = key_stride_tok;

@@ -72,9 +72,10 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-// binary32 -> E4M3FN byte: nearest, ties to even, saturating, NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3fn_from_f32(float q) {
-  uint32_t u = __float_as_uint(q);
+// binary32 -> E4M3FN byte: nearest, ties to even, saturating, NaN -> 0x7F.  Also built
+// for the host, where it is checked against the reference encoder on all 2^32 inputs.
+__host__ __device__ __forceinline__ uint32_t e4m3fn_from_f32(float q) {
+  uint32_t u = __builtin_bit_cast(uint32_t, q);
   uint32_t sign = (u >> 24) & 0x80u;
   uint32_t a = u & 0x7FFFFFFFu;
   if (a > 0x7F800000u) return 0x7Fu;                 // NaN

@@ -74,7 +74,8 @@ def load_library(path: Optional[str] = None):
     lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp, vp]
     lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, sz, vp, vp,
                                 vp, vp]
-    for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append", "attn_merge_lse",
+    for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append",
+                 "attn_merge_lse",
                  "attn_prefill_causal", "attn_verify"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -224,6 +225,9 @@ def _need_kv(key, value, cache: "CacheDesc", tokens: int):
         raise ValueError(f"key must be [{tokens}, {cache.num_kv_heads}, {cache.head_dim_k}] bf16 with a contiguous "
                          "last dim")
     if value is not None:
+        if cache.v_offset < cache.head_dim_k:
+            raise ValueError(f"value columns [{cache.v_offset}, {cache.v_offset + cache.head_dim_v}) overlap the key's "
+                             f"[0, {cache.head_dim_k}): pass value=None when V is part of the K row")
         _need(value, torch.bfloat16, "value")
         if (value.dim() != 3 or tuple(value.shape) != (tokens, cache.num_kv_heads, cache.head_dim_v)
                 or value.stride(2) != 1):

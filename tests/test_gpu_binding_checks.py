@@ -81,3 +81,25 @@ def test_malformed_tensors_are_rejected(up):
     out, lse, _ = pk.decode_splitkv(q, up.desc, up.bt, up.seq_lens, w.softmax_scale, 4)
     ref, ref_lse = oracle_attention(w, up.cache_bytes())
     compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what="decode after rejected calls")
+
+
+def test_value_overlapping_the_key_is_refused(gpu_lib):
+    """The MLA row's V is K's first 512 columns: writing a separate value there would race with the
+    key's store, so the binding (and the C ABI underneath) refuse it; value=None writes the row."""
+    w = workloads.paged_workload("binding_mla", workloads.mla_geom(0, 64), [70], [1], 12, 1 / math.sqrt(576),
+                                 seed=122, std=0.1)
+    u = Uploaded(w)
+    v = torch.zeros(u.key.shape[0], 1, 512, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="overlap"):
+        pk.cache_write(u.key, v, u.slots, u.desc)
+    lib = pk.load_library()
+    import ctypes
+    st = lib.attn_cache_write(ctypes.c_void_p(u.key.data_ptr()), u.key.stride(0), u.key.stride(1),
+                              ctypes.c_void_p(v.data_ptr()), v.stride(0), v.stride(1),
+                              ctypes.c_void_p(u.slots.data_ptr()), u.key.shape[0], ctypes.byref(u.desc.c_struct()),
+                              None)
+    assert st == pk.ops.ATTN_E_INVALID
+    u.write()
+    out, lse, _ = pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, 4)
+    ref, ref_lse = oracle_attention(w, u.cache_bytes())
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what="mla after a refused write")

@@ -1,5 +1,6 @@
 """GPU parity of attn_prefill_causal: chunked causal prefill over the paged cache
 (4096-token chunks, GQA; diffbot MiMo-V2.6-Flash model card, "What the kernels do")."""
+import copy
 import math
 
 import numpy as np
@@ -67,8 +68,10 @@ def test_chunked_equals_one_shot(gpu_lib):
 
 
 def test_chunked_prefill_config(gpu_lib):
-    """32768 tokens written and attended in 8 chunks of 4096 (block size 16); sampled rows
-    of every chunk (its first and last rows, 64 random rows; 256 rows of chunk 0)."""
+    """32768 tokens written and attended in 8 chunks of 4096 (block size 16).  Checked rows: all
+    4096 of chunk 0; in every chunk its first and last row, one random row of every 32-token
+    query tile (the fast kernel's workgroup tile, so every tile rank of the XCD-aware mapping
+    is sampled) and 256 more random rows."""
     log("prefill config: generating")
     w = workloads.prefill_chunks()
     u = Uploaded(w)
@@ -84,12 +87,25 @@ def test_chunked_prefill_config(gpu_lib):
         pk.prefill_causal(u.q[sl], qsl, seq, u.bt, u.desc, w.softmax_scale, C, out=out[sl], out_lse=lse[sl])
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    rows = [np.arange(0, 128), np.arange(C - 128, C)]
+    cache = u.cache_bytes()
+    refs, ref_lses, rows = [], [], []
     for c in range(T // C):
-        rows.append(np.array([c * C, c * C + C - 1]))
-        rows.append(c * C + rng.choice(C, 64, replace=False))
-    rows = np.unique(np.concatenate(rows))
-    log(f"oracle on {len(rows)} rows")
-    ref, ref_lse = oracle_attention(w, u.cache_bytes(), rows=rows)
+        if c == 0:
+            local = np.arange(C)
+        else:
+            local = np.unique(np.concatenate([[0, C - 1], np.arange(0, C, 32) + rng.integers(0, 32, C // 32),
+                                              rng.choice(C, 256, replace=False)]))
+        # the oracle on chunk c alone: its C queries at positions cC..cC+C-1 over keys 0..(c+1)C-1
+        wc = copy.copy(w)
+        wc.q = w.q[c * C: (c + 1) * C]
+        wc.seq_lens = torch.tensor([(c + 1) * C], dtype=torch.int32)
+        wc.query_start_loc = torch.tensor([0, C], dtype=torch.int32)
+        log(f"oracle on {len(local)} rows of chunk {c}")
+        r, rl = oracle_attention(wc, cache, rows=local)
+        refs.append(r)
+        ref_lses.append(rl)
+        rows.append(c * C + local)
+    rows = np.concatenate(rows)
     idx = torch.from_numpy(rows).to(DEV)
-    compare(out[idx], ref, lse_gpu=lse[idx], lse_ref=ref_lse, what="chunked prefill 32768", strict=True)
+    compare(out[idx], np.concatenate(refs), lse_gpu=lse[idx], lse_ref=np.concatenate(ref_lses),
+            what=f"chunked prefill 32768 ({len(rows)} rows)", strict=True)

@@ -1,6 +1,7 @@
 """GPU parity of the attention sink: per query head, one logit that joins each row's
-softmax denominator with no value (diffbot model card, "Known issues": the sink read as an
-extra softmax-denominator logit).  Split-KV entry points add it in the merge (both merge
+softmax denominator with no value (diffbot model card, "Update 2026-10-01: three
+correctness fixes", the item on the vision encoder's sink, read as an extra softmax-denominator
+logit).  Split-KV entry points add it in the merge (both merge
 kernels), prefill in its own normalisation (both prefill kernels).  Every path is checked
 against the oracle with the same sinks; -inf sinks must give exactly the no-sink results;
 a sequence without keys outputs 0 and lse = sink."""

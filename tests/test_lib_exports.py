@@ -74,6 +74,32 @@ def test_cache_write_rejects_bad_descriptors(lib, bad, msg):
     assert msg in lib.attn_last_error().decode()
 
 
+@pytest.mark.parametrize("v_offset,dv", [(0, 512), (64, 128), (191, 8)])
+def test_value_overlapping_key_is_invalid(lib, v_offset, dv):
+    """A value whose columns share bytes with K's (the MLA row, V = K's first columns) would make
+    two threads store one element in no fixed order: rejected, also on the fused decode path."""
+    d = _desc(num_kv_heads=1, row_dim=576, head_dim_k=576 if v_offset == 0 else 192, head_dim_v=dv,
+              v_offset=v_offset, stride_block=16 * 576, stride_slot=576, stride_head=576)
+    st = lib.attn_cache_write(ctypes.c_void_p(0x2000), 576, 576, ctypes.c_void_p(0x4000), dv, dv,
+                              ctypes.c_void_p(0x3000), 3, ctypes.byref(d), None)
+    assert st == ops.ATTN_E_INVALID and "overlap K columns" in lib.attn_last_error().decode()
+    # the same row without a value is accepted up to the launch (no GPU here: checked via a 0-token call)
+    assert lib.attn_cache_write(None, 0, 0, None, 0, 0, None, 0, ctypes.byref(d), None) == ops.ATTN_OK
+    ws = ctypes.c_void_p(0x10000)
+    st = lib.attn_decode_splitkv_append(ctypes.c_void_p(0x2000), 576, 576, 1, 12, ctypes.byref(d),
+                                        ctypes.c_void_p(0x5000), 4, ctypes.c_void_p(0x6000), ctypes.c_float(0.04),
+                                        4, None, ctypes.c_void_p(0x2000), 576, 576, ctypes.c_void_p(0x4000), dv, dv,
+                                        ctypes.c_void_p(0x3000), ws, 1 << 30, None, None, None, None)
+    assert st == ops.ATTN_E_INVALID and "overlap K columns" in lib.attn_last_error().decode()
+
+
+def test_value_after_key_is_accepted_by_the_column_check(lib):
+    """V starting exactly where K ends (the DiffKV row) passes the overlap check: the call gets as
+    far as the 0-token no-op."""
+    d = _desc()
+    assert lib.attn_cache_write(None, 0, 0, ctypes.c_void_p(0x4000), 0, 0, None, 0, ctypes.byref(d), None) == ops.ATTN_OK
+
+
 def test_zero_tokens_is_a_noop_and_null_desc_is_invalid(lib):
     d = _desc()
     assert lib.attn_cache_write(None, 0, 0, None, 0, 0, None, 0, ctypes.byref(d), None) == ops.ATTN_OK
@@ -184,3 +210,4 @@ def test_alignment_and_size_checks(lib):
     assert lib.attn_verify(*vargs(2, ctypes.c_void_p(6 * big + 6))) == ops.ATTN_E_UNSUPPORTED
     # a workspace size past 62 bits is reported as 0 (invalid), not wrapped
     assert lib.attn_splitkv_workspace_bytes(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 20, 4096) == 0
+

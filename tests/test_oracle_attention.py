@@ -224,6 +224,66 @@ def test_partition_ranges_cover_keys_once():
             assert all(lo % 16 == 0 or lo == S for lo, hi in rng)
 
 
+def test_partition_ranges_closed_form():
+    """The 16-key rule the library documents, independent of the block size: C = ceil(S / P)
+    rounded up to 16 (values worked out by hand)."""
+    assert R.partition_ranges(100, 3) == [(0, 48), (48, 96), (96, 100)]
+    assert R.partition_ranges(37, 4) == [(0, 16), (16, 32), (32, 37), (37, 37)]
+    r = R.partition_ranges(100000, 224)                 # 447 keys -> 448
+    assert r[0] == (0, 448) and r[222] == (99456, 99904) and r[223] == (99904, 100000)
+    r = R.partition_ranges(100000, 16)                  # 6250 -> 6256
+    assert r[1] == (6256, 12512) and r[15] == (93840, 100000)
+    r = R.partition_ranges(131072, 128)
+    assert all(hi - lo == 1024 for lo, hi in r)
+    assert R.partition_ranges(5, 7) == [(0, 5)] + [(5, 5)] * 6
+
+
+def _sdpa_range(w, cache, b, lo, hi):
+    """torch fp64 attention of sequence b's query rows over keys [lo, hi) only (explicit mask:
+    key j visible to query i iff j <= S - L + i); returns out [L, Hq, Dv] and lse [L, Hq]."""
+    g = w.geom
+    vals = torch.from_numpy(cache.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    view = vals[: g.cache_elems].view(g.num_blocks, g.block_size, g.num_kv_heads, g.row_dim)
+    qsl = w.query_start_loc.tolist()
+    S, L = int(w.seq_lens[b]), qsl[b + 1] - qsl[b]
+    j = torch.arange(lo, hi)
+    rows = view[w.block_tables[b].long()[j // g.block_size], j % g.block_size]
+    K = rows[..., : g.head_dim_k].transpose(0, 1)                         # [Hkv, n, Dk]
+    V = rows[..., g.v_offset: g.v_offset + g.head_dim_v].transpose(0, 1)
+    G = w.num_q_heads // g.num_kv_heads
+    K, V = K.repeat_interleave(G, 0), V.repeat_interleave(G, 0)           # [Hq, n, D]
+    q = w.q[qsl[b]: qsl[b + 1]].to(torch.float64).transpose(0, 1)        # [Hq, L, Dk]
+    vis = j[None, :] <= (S - L + torch.arange(L))[:, None]                # [L, n]
+    sc = torch.where(vis[None], torch.matmul(q, K.transpose(1, 2)) * w.softmax_scale, -torch.inf)
+    lse = torch.logsumexp(sc, dim=-1)                                     # [Hq, L]
+    out = torch.matmul(torch.softmax(sc, dim=-1), V)
+    return out.transpose(0, 1).numpy(), lse.transpose(0, 1).numpy()
+
+
+@pytest.mark.parametrize("bs,P", [(64, 3), (64, 7), (16, 5)])
+def test_partials_match_torch_per_range(bs, P):
+    """Each exported partial is the attention restricted to its 16-key-rounded range (torch's
+    softmax and logsumexp over an explicit mask), empty ranges give 0 / -inf, whatever BS."""
+    w = small_workload([100, 37, 0], [1, 8, 1], bs=bs, seed=7)   # tokens 29-31 of seq 1 see no key of [32, 37)
+    cache = written_cache(w)
+    qb = w.q.view(torch.int16).numpy().view(np.uint16)
+    po, pl = R.paged_attention_partials(qb, w.query_start_loc.numpy(), w.seq_lens.numpy(),
+                                        w.block_tables.numpy(), cache, spec_of(w), w.softmax_scale, P)
+    qsl = w.query_start_loc.tolist()
+    for b, S in enumerate(w.seq_lens.tolist()):
+        rows = slice(qsl[b], qsl[b + 1])
+        for p, (lo, hi) in enumerate(R.partition_ranges(S, P)):
+            if hi <= lo:
+                assert np.all(po[rows, :, p] == 0) and np.all(np.isneginf(pl[rows, :, p]))
+                continue
+            o, l = _sdpa_range(w, cache, b, lo, hi)
+            fin = np.isfinite(l)
+            assert np.array_equal(np.isneginf(pl[rows, :, p]), ~fin)      # a token whose keys all lie later
+            np.testing.assert_allclose(po[rows, :, p][fin], o[fin], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(pl[rows, :, p][fin], l[fin], rtol=0, atol=1e-12)
+            assert np.all(po[rows, :, p][~fin] == 0)
+
+
 def test_merge_edge_cases():
     po = np.random.default_rng(0).standard_normal((3, 2, 4, 5))
     pl = np.full((3, 2, 4), -np.inf)

@@ -1,6 +1,7 @@
 """Pins of the oracle's attention sink: a per-query-head logit that joins the softmax
-denominator as one more term with no value (diffbot model card, "Known issues": the vision
-encoder's sink read as an extra softmax-denominator logit).
+denominator as one more term with no value (diffbot model card, "Update 2026-10-01: three
+correctness fixes", the item on the vision encoder's sink, read as an extra
+softmax-denominator logit).
   * a -inf sink is no sink, bit for bit;
   * one visible key k against a sink c is a two-way softmax: out = v * sigmoid(s - c) and
     lse = logaddexp(s, c), with s = scale * q.k computed here from the bf16 values;
