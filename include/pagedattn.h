@@ -197,6 +197,32 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
                                 void* out, float* out_lse, const float* sinks, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_decode_splitkv_noalloc -- attn_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and the same results
+ * bit for bit, with the split-KV partials in a fixed workspace that the library
+ * holds in its own device code object (ATTN_NOALLOC_WORKSPACE_BYTES = 16 MiB per
+ * GPU, resident from the first call on that GPU until the process ends).  The
+ * call allocates and frees nothing; the caller still passes q, the cache, the
+ * index arrays and the outputs.
+ *   Arguments as attn_decode_splitkv without workspace / workspace_bytes; out is
+ *   required (NULL with num_seqs > 0 is ATTN_E_INVALID: the partials cannot be
+ *   read back).  A call whose attn_splitkv_workspace_bytes(num_seqs,
+ *   num_q_heads, head_dim_v, num_partitions) exceeds the fixed size returns
+ *   ATTN_E_INVALID before touching the GPU.
+ *   Every call on one GPU shares that GPU's workspace (it keeps the last call's
+ *   partials): calls that overlap on one GPU -- on different streams, or from
+ *   different threads -- race and must be ordered by the caller.  Its contents
+ *   need no initialisation (every partition writes its own partial).        */
+#define ATTN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+attn_status attn_decode_splitkv_noalloc(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        const attn_cache_desc* cache, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, float softmax_scale, int32_t num_partitions,
+                                        const attn_split_policy* policy, void* out, float* out_lse,
+                                        const float* sinks, void* stream);
+
+/* ---------------------------------------------------------------------------
  * attn_decode_splitkv_append -- one decode step with its new token: the result
  * (cache contents, out, out_lse, workspace partials) is that of
  *   attn_cache_write(key, value, slot_mapping, num_tokens = num_seqs)

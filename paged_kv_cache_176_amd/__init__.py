@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     cache_write,
     decode_splitkv,
     decode_splitkv_append,
+    decode_splitkv_noalloc,
     load_library,
     merge_lse,
     new_workspace,

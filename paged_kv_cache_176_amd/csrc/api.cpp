@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <utility>
 
 #include "../../include/pagedattn.h"
@@ -244,6 +245,39 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
   return check_launch(who);
 }
 
+// Split-KV workspace of attn_decode_splitkv_noalloc: a file-scope device array, so that the
+// call allocates nothing.  Each GPU holds its own copy (at its own address) from the first call
+// on it until the process ends.  In host code `scratch` is only a stand-in for the symbol: the
+// device address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or NULL with an error status in *st.
+void* scratch_for_current_device(const char* who, attn_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = fail(ATTN_E_HIP, "%s: no current HIP device (%s)", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *st = fail(ATTN_E_HIP, "%s: hipGetSymbolAddress of the workspace failed on device %d: %s", who, dev,
+                 hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +327,32 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
   return run_splitkv("attn_decode_splitkv", q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1,
                      num_q_heads, cache, block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, policy,
                      workspace, workspace_bytes, out, out_lse, sinks, stream);
+}
+
+attn_status attn_decode_splitkv_noalloc(const void* q, int64_t q_stride_tok, int64_t q_stride_head, int32_t num_seqs,
+                                        int32_t num_q_heads, const attn_cache_desc* cache, const int32_t* block_tables,
+                                        int32_t bt_stride, const int32_t* seq_lens, float softmax_scale,
+                                        int32_t num_partitions, const attn_split_policy* policy, void* out,
+                                        float* out_lse, const float* sinks, void* stream) {
+  const char* who = "attn_decode_splitkv_noalloc";
+  if (!out && num_seqs > 0)
+    return fail(ATTN_E_INVALID, "%s: out is required (the partials stay in the library's own buffer)", who);
+  if (num_seqs > 0 && num_q_heads > 0 && num_partitions > 0 && cache && cache->head_dim_v > 0) {
+    const size_t need = splitkv_bytes(num_seqs, num_q_heads, cache->head_dim_v, num_partitions);
+    if (need == 0 || need > kScratchBytes)
+      return fail(ATTN_E_INVALID, "%s: %d sequences x %d heads x %d partitions x (%d + 1) floats need %zu bytes, "
+                  "over the fixed workspace of %zu bytes", who, num_seqs, num_q_heads, num_partitions,
+                  cache->head_dim_v, need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    attn_status st = ATTN_OK;
+    ws = scratch_for_current_device(who, &st);
+    if (!ws) return st;
+  }
+  return run_splitkv(who, q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1, num_q_heads, cache,
+                     block_tables, bt_stride, seq_lens, softmax_scale, num_partitions, policy, ws, kScratchBytes, out,
+                     out_lse, sinks, stream);
 }
 
 attn_status attn_decode_splitkv_append(const void* q, int64_t q_stride_tok, int64_t q_stride_head,

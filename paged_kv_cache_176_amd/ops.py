@@ -17,7 +17,7 @@ _STATUS = {1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_HIP"}
 KV_BF16, KV_FP8 = 0, 1
 SCALE_NONE, SCALE_TENSOR, SCALE_HEAD = 0, 1, 2
 EXPORTS = ("attn_cache_write", "attn_splitkv_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_append",
-           "attn_merge_lse",
+           "attn_decode_splitkv_noalloc", "attn_merge_lse",
            "attn_prefill_causal", "attn_verify", "attn_last_error", "attn_version")
 
 
@@ -70,12 +70,14 @@ def load_library(path: Optional[str] = None):
     lib.attn_decode_splitkv.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, sz, vp, vp, vp, vp]
     lib.attn_decode_splitkv_append.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, pp,
                                                vp, i64, i64, vp, i64, i64, vp, vp, sz, vp, vp, vp, vp]
+    lib.attn_decode_splitkv_noalloc.argtypes = [vp, i64, i64, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, vp, vp,
+                                                vp]
     lib.attn_merge_lse.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.attn_prefill_causal.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, vp, vp, vp, vp]
     lib.attn_verify.argtypes = [vp, i64, i64, vp, i32, i32, i32, i32, dp, vp, i32, vp, f32, i32, pp, vp, sz, vp, vp,
                                 vp, vp]
     for name in ("attn_cache_write", "attn_decode_splitkv", "attn_decode_splitkv_append",
-                 "attn_merge_lse",
+                 "attn_decode_splitkv_noalloc", "attn_merge_lse",
                  "attn_prefill_causal", "attn_verify"):
         getattr(lib, name).restype = ctypes.c_int
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -346,6 +348,32 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
         _stream(stream)))
     return out, out_lse, ws
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20
+
+
+def decode_splitkv_noalloc(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                           softmax_scale: float, num_partitions: int, out: torch.Tensor,
+                           out_lse: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
+                           split_policy=None, stream=None):
+    """decode_splitkv into caller-given outputs with the library's own fixed workspace: the call
+    allocates nothing (out [B, Hq, Dv] bf16 is required; out_lse [B, Hq] fp32 optional)."""
+    load_library()
+    _need_query(q, cache)
+    B, Hq = q.shape[0], q.shape[1]
+    _need_table(block_tables, B)
+    _need_index(seq_lens, "seq_lens", B)
+    if out is None:
+        raise ValueError("out is required")
+    _need_rows(out, torch.bfloat16, "out", (B, Hq, cache.head_dim_v))
+    _need_rows(out_lse, torch.float32, "out_lse", (B, Hq))
+    d = cache.c_struct()
+    _check(_lib.attn_decode_splitkv_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
+        _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy), _ptr(out), _ptr(out_lse),
+        _sinks(sinks, Hq), _stream(stream)))
+    return out, out_lse
 
 
 def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[torch.Tensor],

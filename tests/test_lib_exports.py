@@ -211,3 +211,18 @@ def test_alignment_and_size_checks(lib):
     # a workspace size past 62 bits is reported as 0 (invalid), not wrapped
     assert lib.attn_splitkv_workspace_bytes(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 20, 4096) == 0
 
+
+def test_noalloc_rejects_sizes_over_its_workspace_before_the_gpu(lib):
+    """attn_decode_splitkv_noalloc checks the partials' size against its fixed 16 MiB workspace
+    before any HIP call (this machine has no GPU): B1 x 32 heads x 1024 partitions x 129 floats
+    = 16.9 MB is refused; a NULL output is refused too."""
+    d = _desc()
+    args = lambda B, P, out: (ctypes.c_void_p(0x2000), 32 * 192, 192, B, 32, ctypes.byref(d), ctypes.c_void_p(0x5000),
+                              64, ctypes.c_void_p(0x6000), ctypes.c_float(0.07), P, None, out, None, None, None)
+    st = lib.attn_decode_splitkv_noalloc(*args(1, 1024, ctypes.c_void_p(0x7000)))
+    assert st == ops.ATTN_E_INVALID and "over the fixed workspace" in lib.attn_last_error().decode()
+    assert lib.attn_splitkv_workspace_bytes(1, 32, 128, 1024) > ops.NOALLOC_WORKSPACE_BYTES
+    assert lib.attn_splitkv_workspace_bytes(1, 32, 128, 1000) <= ops.NOALLOC_WORKSPACE_BYTES
+    st = lib.attn_decode_splitkv_noalloc(*args(1, 64, None))
+    assert st == ops.ATTN_E_INVALID and "out is required" in lib.attn_last_error().decode()
+    assert lib.attn_decode_splitkv_noalloc(*args(0, 64, None)) == ops.ATTN_OK      # nothing to do
