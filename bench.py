@@ -58,6 +58,8 @@ def _copies(nbytes):
 
 
 CUS = 256
+# --partitions with --only: the split count of that one workload (a sweep), else auto
+PARTITIONS_OVERRIDE = 0
 
 
 def auto_partitions(batch, kv_heads, ctx, wgs_per_cu=1, min_keys=256, wave_keys=64):
@@ -67,6 +69,8 @@ def auto_partitions(batch, kv_heads, ctx, wgs_per_cu=1, min_keys=256, wave_keys=
     of wave_keys (one 16-key tile per wave of the workgroup) so that the waves of a
     workgroup get equal tile counts (100K-key MLA at batch 1: 224 partitions of 448 keys
     instead of 256 of 400, whose waves got 7 or 6 tiles)."""
+    if PARTITIONS_OVERRIDE:
+        return PARTITIONS_OVERRIDE
     p = max(1, math.ceil(CUS * wgs_per_cu / max(1, batch * kv_heads)))
     p = min(p, max(1, ctx // min_keys), 4096)
     chunk = math.ceil(math.ceil(ctx / p) / wave_keys) * wave_keys
@@ -111,12 +115,22 @@ class DecodeCase:
         # flops: QK^T and PV over every visible key of every query head
         self.flops = 2 * int(w.seq_lens.sum().item()) * Hq * (g.head_dim_k + g.head_dim_v)
 
-    def partial(self, d):
-        """The step's first kernel: the new token's write and the split-KV partials
-        (attn_decode_splitkv_append with out=NULL; the write rides in the partial kernel)."""
-        self.pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt, self.seq_lens,
-                                      self.w.softmax_scale, self.P, workspace=self.ws, partials_only=True,
-                                      split_policy=self.policy)
+        # every call checked and marshalled once per cache copy: a timed step is one ctypes call
+        # (the binding's per-call Python checks would otherwise sit on the host's critical path
+        # for the shorter steps)
+        self.step_calls = [pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt,
+                                                    self.seq_lens, w.softmax_scale, P, out=self.out, out_lse=self.lse,
+                                                    workspace=self.ws, split_policy=policy, prepare=True)
+                           for d in self.descs]
+        self.partial_calls = [pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt,
+                                                       self.seq_lens, w.softmax_scale, P, workspace=self.ws,
+                                                       partials_only=True, split_policy=policy, prepare=True)
+                              for d in self.descs]
+
+    def partial(self, i):
+        """The step's first kernel on cache copy i: the new token's write and the split-KV
+        partials (attn_decode_splitkv_append with out=NULL; the write rides in the partial kernel)."""
+        self.partial_calls[i % self.ncopy]()
 
     def time_partial(self, reps):
         """Average duration of the partial kernel alone: reps back-to-back launches (each on
@@ -126,21 +140,31 @@ class DecodeCase:
         torch.cuda.synchronize()
         e0.record()
         for i in range(reps):
-            self.partial(self.descs[i % self.ncopy])
+            self.partial(i)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps / 1e3
+
+    def partial_samples(self, reps):
+        """Per-launch durations of the partial kernel (HIP events around each launch; the
+        events' own cost is included, so these sit slightly above the back-to-back average)."""
+        import torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            self.partial(i)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / 1e3 for a, b in evs]
 
     def step(self, i, ev=None):
         """One decode step: attn_decode_splitkv_append with an output buffer -- the new
         token's K/V write and the split-KV partials in one kernel, then the merge (its own
         kernel, or folded into the partial kernel where the shape allows)."""
-        d = self.descs[i % self.ncopy]
         if ev is not None:
             ev[0].record()
-        self.pk.decode_splitkv_append(self.q, self.key, self.value, self.slots, d, self.bt, self.seq_lens,
-                                      self.w.softmax_scale, self.P, out=self.out, out_lse=self.lse,
-                                      workspace=self.ws, split_policy=self.policy)
+        self.step_calls[i % self.ncopy]()
         if ev is not None:
             ev[1].record()
 
@@ -172,44 +196,117 @@ def time_steps(fn, steps, warmup, events=False):
         fn(warmup + i, evs[i])
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    kern = None
+    kern, per = None, None
     if events:
-        kern = sum(a.elapsed_time(b) for a, b in evs) / steps / 1e3
-    return dt, kern
+        per = [a.elapsed_time(b) / 1e3 for a, b in evs]
+        kern = sum(per) / steps
+    return dt, kern, per
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """Time the fp64 oracle on a bounded sample: whole decode steps of the same workload."""
+def pcts(samples_s):
+    """p10 / median / p90 of per-call durations, in microseconds."""
+    import numpy as np
+    a = np.asarray(samples_s, dtype=np.float64) * 1e6
+    return {k: round(float(np.percentile(a, q)), 2) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
+def host_info():
+    """The host the oracle runs on: CPU model, cores this process may use, BLAS threads."""
+    import threadpoolctl
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [x.get("num_threads", 1) for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": max(blas) if blas else 1}
+
+
+def oracle_cache(w, write_new):
+    """The cache image as the oracle sees it: the pre-placed context, and (write_new) the
+    workload's new tokens written by the oracle's cache write."""
     import numpy as np
     import torch
-    import threadpoolctl
     from oracle import paged_ref as R
     import workloads
     g = w.geom
     img = w.cache_init.clone()
-    spec = R.CacheSpec.from_geom(g)
     if "pre_slots" in w.extra:
         workloads.place_bf16_rows(img, g, w.extra["pre_slots"], w.extra["pre_key"], w.extra["pre_value"])
-    base = img.numpy().view(np.uint16)
+    base = img.numpy() if g.kv_dtype == "fp8" else img.numpy().view(np.uint16)
+    if not write_new:
+        return base
     kb = w.key.view(torch.int16).numpy().view(np.uint16)
-    vb = w.value.view(torch.int16).numpy().view(np.uint16)
+    vb = w.value.view(torch.int16).numpy().view(np.uint16) if w.value is not None else None
+    ks = w.k_scale.numpy() if w.k_scale is not None else None
+    vs = w.v_scale.numpy() if w.v_scale is not None else None
+    return R.cache_write(base, R.CacheSpec.from_geom(g), kb, vb, w.slot_mapping.numpy(), ks, vs)
+
+
+def oracle_seconds(w, budget_s, with_write, rows=None):
+    """Wall time of one oracle call on the workload (cache write of the new tokens when
+    with_write, then fp64 attention of `rows`, default every query row), repeated until
+    budget_s has passed; returns (seconds per call, calls)."""
+    import numpy as np
+    import torch
+    from oracle import paged_ref as R
+    spec = R.CacheSpec.from_geom(w.geom)
+    ks = w.k_scale.numpy() if w.k_scale is not None else None
+    vs = w.v_scale.numpy() if w.v_scale is not None else None
     qb = w.q.view(torch.int16).numpy().view(np.uint16)
+    base = oracle_cache(w, write_new=False)
+    written = None if with_write else oracle_cache(w, write_new=True)
+    kb = w.key.view(torch.int16).numpy().view(np.uint16)
+    vb = w.value.view(torch.int16).numpy().view(np.uint16) if w.value is not None else None
     n, t0 = 0, time.perf_counter()
     while True:
-        c = R.cache_write(base, spec, kb, vb, w.slot_mapping.numpy())
+        c = R.cache_write(base, spec, kb, vb, w.slot_mapping.numpy(), ks, vs) if with_write else written
         R.paged_attention(qb, w.query_start_loc.numpy(), w.seq_lens.numpy(), w.block_tables.numpy(), c, spec,
-                          w.softmax_scale)
+                          w.softmax_scale, ks, vs, rows=rows)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = (time.perf_counter() - t0) / n
-    blas = [x.get("num_threads", 1) for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
-    cores = max([len(os.sched_getaffinity(0))] + blas) if blas else len(os.sched_getaffinity(0))
-    return dt, n, min(cores, len(os.sched_getaffinity(0)))
+    return (time.perf_counter() - t0) / n, n
 
 
-def run_prefill(steps, warmup):
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on a bounded sample: whole decode steps of the same workload."""
+    dt, n = oracle_seconds(w, budget_s, with_write=True)
+    info = host_info()
+    return dt, n, min(max(info["blas_threads"], 1), info["affinity_cores"]), info
+
+
+# The oracle timings of the secondary lines run after every GPU measurement: a multithreaded
+# BLAS call right before a timed GPU loop was seen to slow the loop's launches (its threads
+# still spinning), so each line queues its oracle job here and main() runs them at the end.
+DEFERRED = []
+
+
+def defer_cpu(res, seconds_fn, algo, unit, sample, scale=1.0):
+    """Queue an oracle timing whose result lands in res["cpu_oracle"]."""
+    def job():
+        sec, n = seconds_fn()
+        res["cpu_oracle"] = cpu_line(sec, n, algo, unit, sample, scale)
+        return res["cpu_oracle"]
+    DEFERRED.append(job)
+
+
+def cpu_line(seconds, n, algo, unit, sample, scale=1.0):
+    """The oracle's figure for one measured line: `algo` bytes (GB/s) or flops (TFLOP/s) of
+    the whole call, the sampled seconds scaled by `scale` to the whole call."""
+    per_call = seconds * scale
+    value = algo / per_call / (1e9 if unit == "GB/s" else 1e12)
+    return {"value": round(value, 5), "unit": unit, "s_per_call": round(per_call, 3), "calls_timed": n,
+            "sample": sample}
+
+
+def run_prefill(steps, warmup, cpu=True):
     """Chunked prefill of 32768 tokens in 4096-token chunks: write + causal attention per chunk."""
+    import numpy as np
     import torch
     import paged_kv_cache_176_amd as pk
     import workloads
@@ -225,33 +322,58 @@ def run_prefill(steps, warmup):
     qsl = torch.tensor([0, C], dtype=torch.int32, device=dev)
     seqs = [torch.tensor([(c + 1) * C], dtype=torch.int32, device=dev) for c in range(T // C)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T // C)]
-    kern = [0.0] * (T // C)
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T // C)]
 
-    def one(i, _):
+    def one(i, pev):
+        if pev is not None:
+            pev[0].record()
         for c in range(T // C):
             sl = slice(c * C, (c + 1) * C)
+            wev[c][0].record()
             pk.cache_write(key[sl], val[sl], slots[sl], d)
+            wev[c][1].record()
             ev[c][0].record()
             pk.prefill_causal(q[sl], qsl, seqs[c], bt, d, w.softmax_scale, C, out=out[sl], with_lse=False)
             ev[c][1].record()
+        if pev is not None:
+            pev[1].record()
 
-    dt, _ = time_steps(one, steps, warmup)
+    dt, _, _ = time_steps(one, steps, warmup)
     # per-chunk kernel times: median over instrumented passes
-    passes = []
-    for _ in range(max(3, steps)):
+    passes, wpasses, totals = [], [], []
+    for _ in range(max(5, steps)):
         one(0, None)
         torch.cuda.synchronize()
         passes.append([a.elapsed_time(b) / 1e3 for a, b in ev])
+        wpasses.append([a.elapsed_time(b) / 1e3 for a, b in wev])
+        totals.append(sum(passes[-1]))
     kern = [sorted(p[c] for p in passes)[len(passes) // 2] for c in range(T // C)]
+    wmed = float(np.median([x for p in wpasses for x in p]))
     visible = sum((c * C) * C + C * (C + 1) // 2 for c in range(T // C))     # causal pairs per head
     flops = 2 * visible * 32 * (192 + 128)
-    return dict(workload="prefill_32768_in_4096_chunks_bs16", ms_per_pass=dt * 1e3, tflops=flops / dt / 1e12,
-                kernel_ms=sum(kern) * 1e3, kernel_tflops=flops / sum(kern) / 1e12,
-                frac_of_bf16_peak=flops / sum(kern) / 1e12 / BF16_PEAK_TFLOPS,
-                per_chunk_kernel_ms=[round(k * 1e3, 4) for k in kern])
+    chunk_write_bytes = C * 4 * (192 + 128) * 2 * 2          # K/V sources read + cache rows written
+    res = dict(workload="prefill_32768_in_4096_chunks_bs16", ms_per_pass=dt * 1e3, tflops=flops / dt / 1e12,
+               kernel_ms=sum(kern) * 1e3, kernel_tflops=flops / sum(kern) / 1e12,
+               frac_of_bf16_peak=flops / sum(kern) / 1e12 / BF16_PEAK_TFLOPS,
+               kernel_ms_pcts={k: round(v / 1e3, 4) for k, v in pcts(totals).items()},
+               per_chunk_kernel_ms=[round(k * 1e3, 4) for k in kern],
+               cache_write_4096=dict(us=round(wmed * 1e6, 2), bytes=chunk_write_bytes,
+                                     gbs=round(chunk_write_bytes / wmed / 1e9, 1)))
+    if cpu:
+        # the oracle on a 128-query slab of the last chunk (queries 28672..28799 over up to 28800 keys)
+        rows = list(range(7 * C, 7 * C + 128))
+        slab_flops = 2 * 32 * (192 + 128) * sum(r + 1 for r in rows)
+
+        def job():
+            sec, n = oracle_seconds(w, 2.0, with_write=False, rows=rows)
+            line = cpu_line(sec, n, slab_flops, "TFLOP/s", "128 query rows of chunk 7 (all 32 heads), fp64 oracle")
+            line["est_s_whole_prefill"] = round(flops / (line["value"] * 1e12), 1)
+            res["cpu_oracle"] = line
+        DEFERRED.append(job)
+    return res
 
 
-def run_verify(mode, steps, warmup, P):
+def run_verify(mode, steps, warmup, P, cpu=True):
     import torch
     import paged_kv_cache_176_amd as pk
     import workloads
@@ -270,34 +392,59 @@ def run_verify(mode, steps, warmup, P):
     ws = pk.new_workspace(T, 32, 128, P, dev)
     out = torch.empty(T, 32, 128, dtype=torch.bfloat16, device=dev)
 
+    calls = [pk.verify(q, qsl, sl, bt, d, w.softmax_scale, w.max_query_len, P, out=out, workspace=ws,
+                       with_lse=False, prepare=True) for d in descs]
+
     def one(i, ev):
         if ev is not None:
             ev[0].record()
-        pk.verify(q, qsl, sl, bt, descs[i % len(descs)], w.softmax_scale, w.max_query_len, P, out=out,
-                  workspace=ws, with_lse=False)
+        calls[i % len(calls)]()
         if ev is not None:
             ev[1].record()
 
-    dt, _ = time_steps(one, steps, warmup)
-    _, kern = time_steps(one, steps, 0, events=True)
+    dt, _, _ = time_steps(one, steps, warmup)
+    _, kern, per = time_steps(one, steps, 0, events=True)
     kv = 4 * 46080 * 4 * 320
-    return dict(workload=f"fp8_verify_b4_s46080_l4_{mode}", P=P, us_per_call=dt * 1e6, kernel_us=kern * 1e6,
-                kv_gbs=kv / kern / 1e9)
+    res = dict(workload=f"fp8_verify_b4_s46080_l4_{mode}", P=P, us_per_call=round(dt * 1e6, 2),
+               kernel_us=round(kern * 1e6, 2), kernel_us_pcts=pcts(per), kv_gbs=round(kv / kern / 1e9, 1),
+               call_gbs=round(kv / dt / 1e9, 1))
+    if cpu:
+        defer_cpu(res, lambda: oracle_seconds(w, 2.0, with_write=False), kv, "GB/s",
+                  "the whole verify call (4 x 4 query rows + 4 padded rows), fp64 oracle on the fp8 cache bytes")
+    return res
 
 
-def run_mla(batch, steps, warmup):
+def decode_line(c, name, steps, warmup, cpu, cpu_rows=None, cpu_scale=1.0, cpu_sample=None):
+    """Timing of one DecodeCase: event-free steps, an instrumented pass (per-step events),
+    the partial kernel back to back and per launch, and (cpu) the oracle on a sample."""
+    d, _, _ = time_steps(c.step, steps, warmup)
+    _, se, sper = time_steps(c.step, steps, 0, events=True)
+    k = c.time_partial(steps)
+    kper = c.partial_samples(steps)
+    res = dict(workload=name, P=c.P, us_per_step=round(d * 1e6, 2), step_us_events=round(se * 1e6, 2),
+               step_us_events_pcts=pcts(sper), partial_kernel_us=round(k * 1e6, 2),
+               partial_kernel_us_pcts=pcts(kper), kv_gbs=round(c.kv_bytes / k / 1e9, 1),
+               step_gbs=round((c.kv_bytes + c.other_bytes) / d / 1e9, 1),
+               tflops=round(c.flops / k / 1e12, 2))
+    if cpu:
+        w = c.w
+        defer_cpu(res, lambda: oracle_seconds(w, 2.0, with_write=cpu_rows is None, rows=cpu_rows),
+                  c.kv_bytes + c.other_bytes, "GB/s", cpu_sample or "a whole decode step (cache write + fp64 attention)",
+                  cpu_scale)
+    return res
+
+
+def run_mla(batch, steps, warmup, cpu=True):
     import workloads
     p = auto_partitions(batch, 1, 100000)
     c = DecodeCase(workloads.mla_decode(batch, 100000), p)
-    d, _ = time_steps(c.step, steps, warmup)
-    _, se = time_steps(c.step, steps, 0, events=True)
-    k = c.time_partial(steps)
-    return dict(workload=f"mla_b{batch}_s100000_h12", P=p, us_per_step=round(d * 1e6, 2),
-                step_us_events=round(se * 1e6, 2), partial_kernel_us=round(k * 1e6, 2),
-                kv_gbs=round(c.kv_bytes / k / 1e9, 1), tflops=round(c.flops / k / 1e12, 2))
+    if batch == 1:
+        return decode_line(c, "mla_b1_s100000_h12", steps, warmup, cpu)
+    return decode_line(c, f"mla_b{batch}_s100000_h12", steps, warmup, cpu, cpu_rows=[0], cpu_scale=batch,
+                       cpu_sample=f"1 of the {batch} sequences (fp64 attention over its 100000 keys), x{batch}")
 
 
-def run_mla_verify(batch, steps, warmup, qlen=4):
+def run_mla_verify(batch, steps, warmup, qlen=4, cpu=True):
     """MLA verify: qlen query tokens per sequence (drafts + 1) over the 12-head latent
     cache, S = 100000, rotating cache copies; one attn_verify call (partials, then the merge)."""
     import torch
@@ -319,32 +466,35 @@ def run_mla_verify(batch, steps, warmup, qlen=4):
     ws = pk.new_workspace(T, 12, 512, P, dev)
     out = torch.empty(T, 12, 512, dtype=torch.bfloat16, device=dev)
 
+    calls = [pk.verify(q, qsl, sl, bt, d, w.softmax_scale, qlen, P, out=out, workspace=ws, with_lse=False,
+                       prepare=True) for d in descs]
+
     def one(i, ev):
         if ev is not None:
             ev[0].record()
-        pk.verify(q, qsl, sl, bt, descs[i % len(descs)], w.softmax_scale, qlen, P, out=out, workspace=ws,
-                  with_lse=False)
+        calls[i % len(calls)]()
         if ev is not None:
             ev[1].record()
 
-    dt, _ = time_steps(one, steps, warmup)
-    _, kern = time_steps(one, steps, 0, events=True)
+    dt, _, _ = time_steps(one, steps, warmup)
+    _, kern, per = time_steps(one, steps, 0, events=True)
     kv = batch * 100000 * 576 * 2
     flops = 2 * batch * qlen * 12 * 100000 * (576 + 512)
-    return dict(workload=f"mla_verify_b{batch}_s100000_l{qlen}_h12", P=P, us_per_call=round(dt * 1e6, 2),
-                kernel_us=round(kern * 1e6, 2), kv_gbs=round(kv / dt / 1e9, 1), tflops=round(flops / dt / 1e12, 1))
+    res = dict(workload=f"mla_verify_b{batch}_s100000_l{qlen}_h12", P=P, us_per_call=round(dt * 1e6, 2),
+               kernel_us=round(kern * 1e6, 2), kernel_us_pcts=pcts(per), kv_gbs=round(kv / dt / 1e9, 1),
+               tflops=round(flops / dt / 1e12, 1))
+    if cpu:
+        rows = list(range(qlen))
+        defer_cpu(res, lambda: oracle_seconds(w, 2.0, with_write=False, rows=rows), kv, "GB/s",
+                  f"the {qlen} query rows of 1 of the {batch} sequence(s), fp64 oracle, x{batch}", scale=batch)
+    return res
 
 
-def run_decode_extra(b, s, bs, steps, warmup):
+def run_decode_extra(b, s, bs, steps, warmup, cpu=True):
     import workloads
     p = auto_partitions(b, 4, s, wgs_per_cu=2)
     c = DecodeCase(workloads.long_decode(b, s, bs), p)
-    d, _ = time_steps(c.step, steps, warmup)
-    _, se = time_steps(c.step, steps, 0, events=True)
-    k = c.time_partial(steps)
-    return dict(workload=f"decode_b{b}_s{s}_bs{bs}", P=p, us_per_step=round(d * 1e6, 2),
-                step_us_events=round(se * 1e6, 2), partial_kernel_us=round(k * 1e6, 2),
-                kv_gbs=round(c.kv_bytes / k / 1e9, 1), step_gbs=round((c.kv_bytes + c.other_bytes) / d / 1e9, 1))
+    return decode_line(c, f"decode_b{b}_s{s}_bs{bs}", steps, warmup, cpu)
 
 
 # context buckets -> active splits for the mixed decode batch (4 KV heads, two 4-wave
@@ -353,7 +503,7 @@ MIXED_POLICY = [(2048, 4), (8192, 16), (32768, 32), (1 << 30, 64)]
 MIXED_LENS = [131072, 65536, 16384, 8192, 4096, 2048, 1024, 256]
 
 
-def run_decode_mixed(steps, warmup):
+def run_decode_mixed(steps, warmup, cpu=True):
     """Decode over a batch of mixed context lengths: the split policy (launch P 64, active
     splits per sequence from MIXED_POLICY) against fixed split counts for every sequence."""
     import torch
@@ -363,31 +513,117 @@ def run_decode_mixed(steps, warmup):
     res = {"workload": "decode_mixed_b8_bs16", "lens": MIXED_LENS, "policy": MIXED_POLICY}
     for name, P, pol in (("policy_P64", 64, MIXED_POLICY), ("fixed_P16", 16, None), ("fixed_P64", 64, None)):
         c = DecodeCase(w, P, policy=pol)
-        d, _ = time_steps(c.step, steps, warmup)
-        res[name] = dict(us_per_step=round(d * 1e6, 2), kv_gbs=round(c.kv_bytes / d / 1e9, 1))
+        d, _, _ = time_steps(c.step, steps, warmup)
+        _, _, sper = time_steps(c.step, steps, 0, events=True)
+        res[name] = dict(us_per_step=round(d * 1e6, 2), step_us_events_pcts=pcts(sper),
+                         kv_gbs=round(c.kv_bytes / d / 1e9, 1))
+        algo = c.kv_bytes + c.other_bytes
         del c
         torch.cuda.empty_cache()
+    if cpu:
+        defer_cpu(res, lambda: oracle_seconds(w, 2.0, with_write=True), algo, "GB/s",
+                  "a whole decode step of the 8 sequences (cache write + fp64 attention)")
     return res
 
 
+def copy_rate(dev="cuda:0", nbytes=2 << 30, reps=10):
+    """A plain device-to-device copy (torch's copy kernel) of nbytes: (read + write bytes) /
+    median time, the reference rate each HBM-bound line is also quoted against."""
+    import numpy as np
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) / 1e3 for a, b in evs]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "us": round(t * 1e6, 1), "gbs": round(2 * nbytes / t / 1e9, 1),
+            "kernel": "torch device-to-device copy_ of 2 GiB (read + write counted)"}
+
+
+def sample_clocks(fn, seconds=1.5):
+    """Engine clocks while `fn` runs back to back: `amd-smi metric -c` taken once, halfway
+    through a window of `seconds` (current gfx clock of each XCD and the memory clock), or
+    None where the tool is not available."""
+    import subprocess
+    import threading
+    import torch
+    box = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0", "--json"], capture_output=True, text=True,
+                               timeout=20)
+            box["json"] = r.stdout
+        except Exception as e:                       # noqa: BLE001 - the clocks are informative only
+            box["err"] = str(e)
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end or th.is_alive():
+        fn(i, None)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    th.join()
+    return parse_clocks(box.get("json"))
+
+
+def parse_clocks(text):
+    """gfx clocks (MHz) of every XCD and the memory clock from amd-smi's JSON, or None."""
+    if not text:
+        return None
+    try:
+        d = json.loads(text)
+        d = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+        clk = d["clock"]
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+    gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)
+           and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+    mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v, dict)
+           and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+    if not gfx:
+        return None
+    return {"gfx_mhz_per_xcd": gfx, "gfx_mhz_mean": round(sum(gfx) / len(gfx), 1), "mem_mhz": mem[0] if mem else None,
+            "source": "amd-smi metric -c, sampled mid-run"}
+
+
 def run_only(name, steps, warmup):
+    """One secondary workload alone, without the oracle (the profiling commands)."""
     if name == "prefill":
-        return run_prefill(max(1, min(steps, 5)), max(1, min(warmup, 3)))
+        return run_prefill(max(1, min(steps, 5)), max(1, min(warmup, 3)), cpu=False)
     if name == "fp8_verify":
-        return run_verify("tensor", steps, warmup, auto_partitions(4, 4, 46080))
+        return run_verify("tensor", steps, warmup, auto_partitions(4, 4, 46080), cpu=False)
     if name == "mla_b1":
-        return run_mla(1, steps, warmup)
+        return run_mla(1, steps, warmup, cpu=False)
     if name == "mla_b16":
-        return run_mla(16, steps, warmup)
+        return run_mla(16, steps, warmup, cpu=False)
+    if name == "mla_verify_b1":
+        return run_mla_verify(1, steps, warmup, cpu=False)
     if name == "mla_verify_b16":
-        return run_mla_verify(16, steps, warmup)
+        return run_mla_verify(16, steps, warmup, cpu=False)
     if name == "decode_mixed":
-        return run_decode_mixed(steps, warmup)
-    return run_decode_extra(8, 8192, 16, steps, warmup)
+        return run_decode_mixed(steps, warmup, cpu=False)
+    if name == "copy":
+        return copy_rate()
+    return run_decode_extra(8, 8192, 16, steps, warmup, cpu=False)
 
 
 def main():
-    global SPINUP_MS
+    global SPINUP_MS, PARTITIONS_OVERRIDE
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -395,9 +631,11 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="split count (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock sample")
     ap.add_argument("--spinup-ms", type=float, default=SPINUP_MS,
                     help="untimed running of each measured step before its warmup steps (GPU clock spin-up)")
-    ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "mla_verify_b16", "decode_mixed", "decode_b8"], default=None,
+    ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "mla_verify_b1", "mla_verify_b16",
+                             "decode_mixed", "decode_b8", "copy"], default=None,
                     help="run just this secondary workload and print its JSON line (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
@@ -415,7 +653,11 @@ def main():
     pk.load_library()
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.only:
-        print(json.dumps(run_only(args.only, args.steps, args.warmup)), flush=True)
+        PARTITIONS_OVERRIDE = args.partitions
+        res = run_only(args.only, args.steps, args.warmup)
+        if args.copy_probe_mib:
+            res["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
+        print(json.dumps(res), flush=True)
         return
 
     B, S, BS = 1, 131072, 16
@@ -424,11 +666,14 @@ def main():
     case = DecodeCase(w, P)
     # the timed steps (nothing but the step's kernels between the synchronisations); then,
     # outside the timed region, the partial kernel alone launched back to back (its
-    # duration for the roofline) and a pass with HIP events around each step (the per-step
-    # device figure, which carries the events' own overhead)
-    dt, _ = time_steps(case.step, args.steps, args.warmup)
+    # duration for the roofline) and per launch (its spread), a pass with HIP events around
+    # each step (the per-step device figure, which carries the events' own overhead), and the
+    # engine clocks while the step runs back to back
+    dt, _, _ = time_steps(case.step, args.steps, args.warmup)
     kern = case.time_partial(args.steps)
-    _, step_ev = time_steps(case.step, min(args.steps, 50), 0, events=True)
+    kper = case.partial_samples(max(args.steps, 20))
+    _, step_ev, sper = time_steps(case.step, max(min(args.steps, 50), 20), 0, events=True)
+    clocks = None if args.no_clocks else sample_clocks(case.step)
     algo = case.kv_bytes + case.other_bytes
     value = algo / dt / 1e9
     achieved = case.kv_bytes / kern / 1e9
@@ -454,41 +699,65 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": MEASURED_TRAFFIC.get((_kernel_source_hash(), P)),
                      "kernel": "splitkv_dma_kernel<192,128,192,1 row group,2 stages,bf16,nontemporal>",
-                     "kernel_us": round(kern * 1e6, 3), "step_us_with_events": round(step_ev * 1e6, 3),
+                     "kernel_us": round(kern * 1e6, 3), "kernel_us_per_launch_pcts": pcts(kper),
+                     "step_us_with_events": round(step_ev * 1e6, 3), "step_us_with_events_pcts": pcts(sper),
                      "algorithmic_bytes_per_launch": case.kv_bytes},
+        "clocks": clocks,
     }
-    if not args.no_cpu_baseline:
-        cdt, n, cores = cpu_baseline(w)
-        line["cpu_baseline"] = {"value": round(algo / cdt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                                "sample": f"{n} whole decode step(s) of the same workload (cache write + fp64 "
-                                          f"attention over all 131072 keys), {cdt:.2f} s each"}
+    del case
+    torch.cuda.empty_cache()
+    copy = copy_rate()
+    line["copy_reference"] = copy
+    line["roofline"]["frac_of_copy"] = round(achieved / copy["gbs"], 4)
+    line["config"]["frac_of_copy"] = round(value / copy["gbs"], 4)
     if not args.no_extra:
+        cpu = not args.no_cpu_baseline
         extra = {}
         for (b2, s2, bs2) in [(1, 131072, 64), (8, 8192, 16), (8, 8192, 64)]:
-            extra[f"decode_b{b2}_s{s2}_bs{bs2}"] = run_decode_extra(b2, s2, bs2, 100, 10)
+            extra[f"decode_b{b2}_s{s2}_bs{bs2}"] = run_decode_extra(b2, s2, bs2, 100, 10, cpu=cpu)
             torch.cuda.empty_cache()
         for b2 in (1, 16):
-            extra[f"mla_b{b2}_s100000_h12"] = run_mla(b2, 50, 5)
+            extra[f"mla_b{b2}_s100000_h12"] = run_mla(b2, 50, 5, cpu=cpu)
             torch.cuda.empty_cache()
-        extra["decode_mixed_b8_bs16"] = run_decode_mixed(100, 10)
+        extra["decode_mixed_b8_bs16"] = run_decode_mixed(100, 10, cpu=cpu)
         torch.cuda.empty_cache()
         for b2 in (1, 16):
-            extra[f"mla_verify_b{b2}_s100000_l4_h12"] = run_mla_verify(b2, 50, 5)
+            extra[f"mla_verify_b{b2}_s100000_l4_h12"] = run_mla_verify(b2, 50, 5, cpu=cpu)
             torch.cuda.empty_cache()
         for mode in ("tensor", "head"):
-            extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, auto_partitions(4, 4, 46080))
-        extra["prefill"] = run_prefill(5, 3)
+            extra[f"fp8_verify_{mode}"] = run_verify(mode, 100, 10, auto_partitions(4, 4, 46080), cpu=cpu)
+        extra["prefill"] = run_prefill(5, 3, cpu=cpu)
+        for v in extra.values():                       # each HBM-bound line against the copy rate
+            if "kv_gbs" in v:
+                v["kv_frac_of_copy"] = round(v["kv_gbs"] / copy["gbs"], 4)
         line["extra"] = extra
         torch.cuda.empty_cache()
+    # the oracle, after every GPU measurement: the headline's baseline, then the other lines'
+    if not args.no_cpu_baseline:
+        cdt, n, cores, info = cpu_baseline(w)
+        line["cpu_baseline"] = {"value": round(algo / cdt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                                "sample": f"{n} whole decode step(s) of the same workload (cache write + fp64 "
+                                          f"attention over all 131072 keys), {cdt:.2f} s each",
+                                **info}
+        for job in DEFERRED:
+            job()
+        DEFERRED.clear()
     if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_probe_bytes"] = n
+        line["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(mib):
+    """One device-to-device copy of `mib` MiB after the measured work: a kernel of known size
+    whose counter readings calibrate FETCH_SIZE / WRITE_SIZE in a profiled run."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 if __name__ == "__main__":

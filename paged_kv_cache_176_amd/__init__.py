@@ -7,6 +7,7 @@ and streams.  If the library is missing the calls raise: there is no fallback.
 """
 from .ops import (  # noqa: F401
     AttnError,
+    PreparedCall,
     CacheDesc,
     cache_write,
     decode_splitkv,

@@ -110,6 +110,28 @@ __device__ __forceinline__ u32x2 bf16x8_to_e4m3fn(u32x4 x, float scale) {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Split-KV partials (fp32, written once by a partial kernel, read once by the merge).
+// WT: write-through stores (sc0 sc1 -- the line goes to memory at once instead of staying
+// dirty in the XCD's L2 for the end of the kernel to write back).  Measured: it pays where a
+// workgroup leaves large partials (MLA: 12 rows x 512 floats, 24.6 KB; the 32-row verify
+// kernels) and costs a little where they are small (the DiffKV decode's 8 rows x 128), so the
+// kernels choose.  Plain nontemporal stores measured slower everywhere.
+template <bool WT>
+__device__ __forceinline__ void store_partial4(float* p, f32x4 v) {
+  if constexpr (WT) asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+  else *reinterpret_cast<f32x4*>(p) = v;
+}
+template <bool WT>
+__device__ __forceinline__ void store_partial1(float* p, float v) {
+  if constexpr (WT) asm volatile("global_store_dword %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+  else *p = v;
+}
+// The merge reads each partial once: nontemporal loads.
+__device__ __forceinline__ f32x4 load_partial4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ float load_partial1(const float* p) { return __builtin_nontemporal_load(p); }
+
 // Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4 with the
 // nontemporal hint): lane i's bytes land at lds_base + 16*i, lds_base wave-uniform.
 // Inline asm on purpose: the compiler's wait-count pass does not know which LDS reads
@@ -161,5 +183,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
+__device__ __forceinline__ int64_t load_uniform64(const int64_t* p) {
+  return *(const __attribute__((address_space(4))) int64_t*)p;
+}
+
+// Zeros in device memory: the target of a kernel's prologue loads whose pointer argument
+// is NULL, so that every per-sequence scalar can be loaded unconditionally (one memory
+// round trip for all of them instead of a dependent chain through branches).
+static __device__ const int64_t kZeroScalars[2] = {0, 0};
 
 }  // namespace pa

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
     const int64_t tok = q0 + qi, head = kvh * G + hh;
     f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
     for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
-    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
+    store_partial4<false>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4, v);
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, (FP8 && NR == 2) ? 2 : 1) void splitkv_par
         for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
       const float lse = (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2;
       const int64_t tok = q0 + qi, head = kvh * G + hh;
-      a.part_lse[(tok * Hq + head) * P + part] = lse;
+      store_partial1<false>(a.part_lse + (tok * Hq + head) * P + part, lse);
     }
   }
 }
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int p = grp + k * NG;
-    pre[k] = (col_ok && p < Pa) ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    pre[k] = (col_ok && p < Pa) ? load_partial4(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float* lse = a.part_lse + rh * P;
   float mx = kNegInf;
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     if (p < Pa) acc += pre[k] * wsh[p];
   }
   if (col_ok)
-    for (int p = grp + PRE * NG; p < Pa; p += NG) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) * wsh[p];
+    for (int p = grp + PRE * NG; p < Pa; p += NG) acc += load_partial4(po + (int64_t)p * DV) * wsh[p];
   gs[grp][slot] = acc;
   __syncthreads();
   if (threadIdx.x < SLOTS && c4 * 4 < DV) {
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(64) void merge_few_kernel(MergeArgs a) {
   f32x4 op[PMAX];
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
-    lp[p] = p < Pa ? lse[p] : kNegInf;
-    op[p] = p < Pa ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    lp[p] = p < Pa ? load_partial1(lse + p) : kNegInf;
+    op[p] = p < Pa ? load_partial4(po + (int64_t)p * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float M = kNegInf;
 #pragma unroll

@@ -71,9 +71,15 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int n = lane & 15, g = lane >> 4;
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const int S = a.seq_lens[b];
-  const int q0 = a.qsl ? a.qsl[b] : b;
-  const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
+  // every per-sequence scalar in one round trip (NULL arguments read zeros): the block ids
+  // of the first tiles wait on seq_len, and nothing else should sit in front of them
+  const int32_t* qslp = a.qsl ? a.qsl + b : reinterpret_cast<const int32_t*>(kZeroScalars);
+  const int64_t* aslp = a.aslot ? a.aslot + b : kZeroScalars;
+  const int S = load_uniform(a.seq_lens + b);
+  const int qs0 = load_uniform(qslp), qs1 = load_uniform(qslp + 1);
+  const int64_t new_slot = a.aslot ? load_uniform64(aslp) : -1;
+  const int q0 = a.qsl ? qs0 : b;
+  const int L = a.qsl ? qs1 - qs0 : 1;
   const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), TT) * TT;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
@@ -81,37 +87,6 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int bs_shift = __builtin_ctz(a.c.block_size);
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
-
-  // ---- fused new-token write (decode): the workgroup whose key range holds key S-1
-  // (partition 0 when S == 0) writes token b's K/V row of this KV head into its slot and
-  // waits for the stores before any of its waves issues a read; no other workgroup
-  // reads that key ----
-  if (a.aslot) {
-    const int64_t slot = a.aslot[b];
-    const bool mine = S > 0 ? (start <= S - 1 && S - 1 < end) : part == 0;
-    if (mine && slot >= 0) {                     // workgroup-uniform
-      const int nk = DK / 8, nv = a.av ? DV / 8 : 0;
-      const int64_t blk = slot / a.c.block_size;
-      const int64_t row = blk * a.c.sb + (slot - blk * a.c.block_size) * a.c.ss + (int64_t)kvh * a.c.sh;
-      for (int i = threadIdx.x; i < nk + nv; i += NW * 64) {
-        const bool isk = i < nk;
-        const int e0 = (isk ? i : i - nk) * 8;
-        const uint16_t* src = isk ? a.ak + (int64_t)b * a.ak_st + (int64_t)kvh * a.ak_sh + e0
-                                  : a.av + (int64_t)b * a.av_st + (int64_t)kvh * a.av_sh + e0;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-        const int64_t el = row + (isk ? 0 : VOFF) + e0;
-        if constexpr (FP8) {
-          const float* sp = isk ? a.c.k_scale : a.c.v_scale;
-          const float sc = a.c.scale_mode == 2 ? sp[kvh] : sp[0];
-          *reinterpret_cast<u32x2*>(a.c.data + el) = bf16x8_to_e4m3fn(x, sc);
-        } else {
-          *reinterpret_cast<u32x4*>(a.c.data + el * 2) = x;
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): the row is in L2
-      __syncthreads();
-    }
-  }
 
   char* ring = smem + wave * WAVE_BYTES;
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
@@ -153,6 +128,41 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 #pragma unroll
   for (int k = 0; k < NST; ++k)
     if (wave + k * NW < nt) issue(wave + k * NW, k);
+
+  // ---- fused new-token write (decode): the workgroup whose key range holds key S-1
+  // (partition 0 when S == 0) owns token b's K/V row of this KV head.  Its lanes load the
+  // row (chunk c of the row as it lies in the cache: lane c % 64), store it into the slot
+  // after the prologue's wait, and the wave that consumes the last tile copies it into
+  // that tile's LDS stage over whatever the DMA fetched for key S-1 (and for the keys past
+  // the partition, which re-read key S-1): the LDS then holds exactly what it would after
+  // a completed write, and no read waits on the store ----
+  constexpr int RCH = (CH + 63) / 64;
+  const bool own = new_slot >= 0 && (S > 0 ? (start <= S - 1 && S - 1 < end) : part == 0);   // uniform
+  u32x4 nrow[RCH];
+#pragma unroll
+  for (int r = 0; r < RCH; ++r) nrow[r] = u32x4{0, 0, 0, 0};
+  if (own) {
+    constexpr int KCH = DK * ESZ / 16;           // chunks of the row that are K
+#pragma unroll
+    for (int r = 0; r < RCH; ++r) {
+      const int c = lane + 64 * r;
+      if (c < CH) {
+        const bool isk = c < KCH;
+        const int e0 = (isk ? c : c - KCH) * (16 / ESZ);   // first element of the chunk
+        const uint16_t* src = isk ? a.ak + (int64_t)b * a.ak_st + (int64_t)kvh * a.ak_sh + e0
+                                  : a.av + (int64_t)b * a.av_st + (int64_t)kvh * a.av_sh + e0;
+        if constexpr (FP8) {
+          const float* sp = isk ? a.c.k_scale : a.c.v_scale;
+          const float sc = a.c.scale_mode == 2 ? sp[kvh] : sp[0];
+          const u32x2 lo = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src), sc);
+          const u32x2 hi2 = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src + 8), sc);
+          nrow[r] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+        } else {
+          nrow[r] = *reinterpret_cast<const u32x4*>(src);
+        }
+      }
+    }
+  }
 
   // ---- Q rows (B operand), visibility limits ----
   bf16x8 qreg[NR][KS];
@@ -233,6 +243,25 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   // count DMA instructions only, and the compiler, which counts only the loads it
   // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
+  if (own && wave == 0) {                        // the new row into its cache slot
+    const int64_t blk = new_slot / a.c.block_size;
+    uint8_t* row = a.c.data + (blk * a.c.sb + (new_slot - blk * a.c.block_size) * a.c.ss + (int64_t)kvh * a.c.sh) * ESZ;
+#pragma unroll
+    for (int r = 0; r < RCH; ++r)
+      if (lane + 64 * r < CH) *reinterpret_cast<u32x4*>(row + (lane + 64 * r) * 16) = nrow[r];
+  }
+  // the last tile's LDS rows from key S-1 on: the new row (see above)
+  auto patch_new_row = [&](int stage, int k) {
+    char* buf = ring + stage * TILE_BYTES;
+    for (int kk = k; kk < TT; ++kk) {
+      const int sw = FP8 ? sd_swz4(kk) : sd_swz(kk);
+#pragma unroll
+      for (int r = 0; r < RCH; ++r) {
+        const int c = lane + 64 * r;
+        if (c < CH) *reinterpret_cast<u32x4*>(buf + (kk * CH + (c ^ sw)) * 16) = nrow[r];
+      }
+    }
+  };
 
   auto compute = [&](int ti, int stage) {
     char* buf = ring + stage * TILE_BYTES;
@@ -348,6 +377,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       else if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
       else if (later >= 1) wait_vm<NINS>();
       else wait_vm<0>();
+      if (own && ti == nt - 1) patch_new_row(stage, S - 1 - (start + ti * TT));   // wave-uniform
       compute(ti, stage);
       stage = (stage + 1) % NST;
     }
@@ -396,7 +426,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     const int64_t tok = q0 + qi, head = kvh * G + hh;
     f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
     for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
-    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
+    store_partial4<(DK > 256)>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4, v);
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;
@@ -407,8 +437,8 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       if (M != kNegInf)
         for (int w = 0; w < NW; ++w) Ls += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - M);
       const int64_t tok = q0 + qi, head = kvh * G + hh;
-      a.part_lse[(tok * Hq + head) * P + part] =
-          (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2;
+      store_partial1<(DK > 256)>(a.part_lse + (tok * Hq + head) * P + part,
+                     (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2);
     }
   }
 }

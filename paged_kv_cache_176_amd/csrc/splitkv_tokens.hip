@@ -70,9 +70,12 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   const int tw = wave & (NTOK - 1), h = wave / NTOK;   // token slot, key half
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const int S = a.seq_lens[b];
-  const int q0 = a.qsl ? a.qsl[b] : b;
-  const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
+  // the per-sequence scalars in one round trip (a NULL qsl reads zeros)
+  const int32_t* qslp = a.qsl ? a.qsl + b : reinterpret_cast<const int32_t*>(kZeroScalars);
+  const int S = load_uniform(a.seq_lens + b);
+  const int qs0 = load_uniform(qslp), qs1 = load_uniform(qslp + 1);
+  const int q0 = a.qsl ? qs0 : b;
+  const int L = a.qsl ? qs1 - qs0 : 1;
   const int Lq = min(L, a.max_q);
   if (tg * NTOK >= Lq) return;                     // no token of this sequence here (uniform)
   const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
@@ -263,9 +266,9 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const f32x4 o1 = *reinterpret_cast<const f32x4*>(slab + n * SLAB_PITCH + db * 16 + 4 * g);
-      *reinterpret_cast<f32x4*>(dst + db * 16) = (acc[db] * a0 + o1 * a1) * f;
+      store_partial4<true>(dst + db * 16, (acc[db] * a0 + o1 * a1) * f);
     }
-    if (g == 0) a.part_lse[rh * P + part] = empty ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2;
+    if (g == 0) store_partial1<true>(a.part_lse + rh * P + part, empty ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2);
   }
 }
 

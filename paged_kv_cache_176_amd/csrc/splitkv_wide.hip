@@ -67,9 +67,12 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int n = lane & 31, g = lane >> 5;        // MFMA column (query row) and k-group
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
-  const int S = a.seq_lens[b];
-  const int q0 = a.qsl ? a.qsl[b] : b;
-  const int L = a.qsl ? a.qsl[b + 1] - q0 : 1;
+  // the per-sequence scalars in one round trip (a NULL qsl reads zeros)
+  const int32_t* qslp = a.qsl ? a.qsl + b : reinterpret_cast<const int32_t*>(kZeroScalars);
+  const int S = load_uniform(a.seq_lens + b);
+  const int qs0 = load_uniform(qslp), qs1 = load_uniform(qslp + 1);
+  const int q0 = a.qsl ? qs0 : b;
+  const int L = a.qsl ? qs1 - qs0 : 1;
   const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     const int64_t tok = q0 + rq, head = kvh * G + rh;
     f32x4 v = *reinterpret_cast<const f32x4*>(slab + r * MERGE_PITCH + c4 * 4);
     for (int w = 1; w < NW; ++w) v += *reinterpret_cast<const f32x4*>(slab + (w * ROWS + r) * MERGE_PITCH + c4 * 4);
-    *reinterpret_cast<f32x4*>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4) = v;
+    store_partial4<true>(a.part_out + ((tok * Hq + head) * P + part) * DV + c4 * 4, v);
   }
   if (threadIdx.x < ROWS) {
     const int r = threadIdx.x;
@@ -324,7 +327,8 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
       if (Mx != kNegInf)
         for (int w = 0; w < NW; ++w) Lx += lw[w * ROWS + r] * fast_exp2(mw[w * ROWS + r] - Mx);
       const int64_t tok = q0 + rq, head = kvh * G + rh;
-      a.part_lse[(tok * Hq + head) * P + part] = (Mx == kNegInf || Lx == 0.f) ? kNegInf : (Mx + __builtin_log2f(Lx)) * kLn2;
+      store_partial1<true>(a.part_lse + (tok * Hq + head) * P + part,
+                     (Mx == kNegInf || Lx == 0.f) ? kNegInf : (Mx + __builtin_log2f(Lx)) * kLn2);
     }
   }
 }

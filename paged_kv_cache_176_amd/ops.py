@@ -92,6 +92,25 @@ def _check(st: int):
         raise AttnError(st, _lib.attn_last_error().decode())
 
 
+class PreparedCall:
+    """One library call whose argument checks and marshalling are done: calling it enqueues
+    the same call again (same tensors, same stream) at the cost of one ctypes call.  For loops
+    that replay a step on unchanged buffers (their contents may change, their storage may
+    not); the tensors it was built from are kept alive.  Its results live in ``out``,
+    ``out_lse`` and ``workspace``."""
+
+    __slots__ = ("_fn", "_args", "_keep", "out", "out_lse", "workspace")
+
+    def __init__(self, fn, args, keep, out=None, out_lse=None, workspace=None):
+        self._fn, self._args, self._keep = fn, args, keep
+        self.out, self.out_lse, self.workspace = out, out_lse, workspace
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != ATTN_OK:
+            raise AttnError(st, _lib.attn_last_error().decode())
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -382,9 +401,10 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
                           out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, partials_only: bool = False,
                           with_lse: bool = True, sinks: Optional[torch.Tensor] = None, split_policy=None,
-                          stream=None):
+                          stream=None, prepare: bool = False):
     """cache_write(key [B, Hkv, Dk], value [B, Hkv, Dv] or None, slot_mapping [B]) followed by
-    decode_splitkv, as one call (the write rides in the decode kernel where it can)."""
+    decode_splitkv, as one call (the write rides in the decode kernel where it can).
+    prepare=True checks and marshals without calling, and returns a PreparedCall."""
     load_library()
     _need_query(q, cache)
     B, Hq = q.shape[0], q.shape[1]
@@ -400,14 +420,18 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
     if not partials_only and with_lse and out_lse is None:
         out_lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     d = cache.c_struct()
-    _check(_lib.attn_decode_splitkv_append(
+    args = (
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
-        _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy),
+        _ptr(seq_lens), ctypes.c_float(softmax_scale), num_partitions, _policy(split_policy),
         _ptr(key), key.stride(0), key.stride(1),
         _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
         _ptr(slot_mapping), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
-        _stream(stream)))
+        _stream(stream))
+    if prepare:
+        return PreparedCall(_lib.attn_decode_splitkv_append, args,
+                            (q, key, value, slot_mapping, block_tables, seq_lens, sinks, d), out, out_lse, ws)
+    _check(_lib.attn_decode_splitkv_append(*args))
     return out, out_lse, ws
 
 
@@ -459,7 +483,9 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
            cache: CacheDesc, softmax_scale: float, max_query_len: int, num_partitions: int,
            out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, partials_only: bool = False, with_lse: bool = True,
-           sinks: Optional[torch.Tensor] = None, split_policy=None, stream=None):
+           sinks: Optional[torch.Tensor] = None, split_policy=None, stream=None, prepare: bool = False):
+    """Multi-token verify (split-KV): q [T, Hq, Dk] -> (out [T, Hq, Dv] bf16, lse [T, Hq], workspace).
+    prepare=True checks and marshals without calling, and returns a PreparedCall."""
     load_library()
     _need_query(q, cache)
     T, Hq = q.shape[0], q.shape[1]
@@ -472,10 +498,14 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
     if not partials_only and with_lse and out_lse is None:
         out_lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
     d = cache.c_struct()
-    _check(_lib.attn_verify(
+    args = (
         _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
-        ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
+        ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), ctypes.c_float(softmax_scale),
         num_partitions, _policy(split_policy), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
-        _stream(stream)))
+        _stream(stream))
+    if prepare:
+        return PreparedCall(_lib.attn_verify, args, (q, query_start_loc, seq_lens, block_tables, sinks, d), out,
+                            out_lse, ws)
+    _check(_lib.attn_verify(*args))
     return out, out_lse, ws

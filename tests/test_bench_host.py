@@ -47,3 +47,30 @@ def test_spinup_flag_is_accepted():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        cwd=ROOT, timeout=120)
     assert r.returncode == 0 and "--spinup-ms" in r.stdout
+
+
+def test_parse_clocks_reads_every_xcd_and_the_memory_clock():
+    import json
+    import bench
+    doc = {"gpu_data": [{"gpu": 0, "clock": {
+        **{f"gfx_{i}": {"clk": {"value": 2100 + i, "unit": "MHz"}, "max_clk": {"value": 2400, "unit": "MHz"}}
+           for i in range(8)},
+        "mem_0": {"clk": {"value": 2000, "unit": "MHz"}}, "vclk_0": {"clk": {"value": 29, "unit": "MHz"}}}}]}
+    c = bench.parse_clocks(json.dumps(doc))
+    assert c["gfx_mhz_per_xcd"] == [2100 + i for i in range(8)] and c["mem_mhz"] == 2000
+    assert c["gfx_mhz_mean"] == 2103.5
+    assert bench.parse_clocks(None) is None and bench.parse_clocks("not json") is None
+
+
+def test_oracle_timing_helpers_on_the_tiny_workload():
+    import bench
+    import workloads
+    w = workloads.tiny()
+    sec, n = bench.oracle_seconds(w, 0.01, with_write=True)
+    assert sec > 0 and n >= 1
+    line = bench.cpu_line(sec, n, 1e9, "GB/s", "tiny", scale=2.0)
+    assert line["s_per_call"] == round(2 * sec, 3) and line["unit"] == "GB/s"
+    info = bench.host_info()
+    assert info["affinity_cores"] >= 1 and info["blas_threads"] >= 1
+    p = bench.pcts([1e-6, 2e-6, 3e-6])
+    assert p["p50"] == 2.0 and p["p10"] < p["p50"] < p["p90"]

@@ -101,3 +101,38 @@ def test_fp8_wide_rows_append(gpu_lib, G):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     ref, ref_lse = oracle_attention(w, ub.cache_bytes())
     compare(o1, ref, fp8=True, lse_gpu=l1, lse_ref=ref_lse, what=f"fp8 G {G} append")
+
+
+def test_prepared_calls_replay_the_direct_calls(gpu_lib):
+    """A PreparedCall (checks and marshalling done once) enqueues the same call again: its
+    outputs equal the direct call's bit for bit, and a replay after the query is rewritten
+    in place follows the new contents (the same storage, new values)."""
+    w = workloads.paged_workload("prep", workloads.diffkv_geom(0, 16), [700, 33, 1], [1, 1, 1], 32,
+                                 1 / math.sqrt(192), seed=131)
+    u = Uploaded(w)
+    setup, (key, value, slots) = split_last_keys(w, u)
+    pk.cache_write(setup[0], setup[1], setup[2], u.desc)
+    call = pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens, w.softmax_scale, 7,
+                                    prepare=True)
+    assert isinstance(call, pk.PreparedCall)
+    call()
+    ref_out, ref_lse, _ = pk.decode_splitkv_append(u.q, key, value, slots, u.desc, u.bt, u.seq_lens,
+                                                   w.softmax_scale, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(call.out, ref_out) and torch.equal(call.out_lse, ref_lse)
+    u.q.mul_(-1)                                   # new contents, same storage
+    call()
+    new_out, new_lse, _ = pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(call.out, new_out) and torch.equal(call.out_lse, new_lse)
+    assert not torch.equal(new_out, ref_out)
+    # verify
+    wv = workloads.paged_workload("prepv", workloads.diffkv_geom(0, 16, kv_dtype="fp8"), [500, 40], [4, 4], 32,
+                                  1 / math.sqrt(192), seed=132, scale_mode="head")
+    uv = Uploaded(wv)
+    uv.write()
+    vcall = pk.verify(uv.q, uv.qsl, uv.seq_lens, uv.bt, uv.desc, wv.softmax_scale, wv.max_query_len, 5, prepare=True)
+    vcall()
+    o, l, _ = pk.verify(uv.q, uv.qsl, uv.seq_lens, uv.bt, uv.desc, wv.softmax_scale, wv.max_query_len, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(vcall.out, o) and torch.equal(vcall.out_lse, l)
