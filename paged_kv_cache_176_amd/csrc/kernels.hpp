@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace pa {
 
 struct CacheView {
@@ -64,6 +66,28 @@ struct SplitArgs {
   const uint16_t* ak; int64_t ak_st, ak_sh;
   const uint16_t* av; int64_t av_st, av_sh;
 };
+
+// Partials of a workgroup whose key range is empty (a sequence with no keys, a partition past
+// its end, or one a split policy leaves unused): output 0 and lse -inf for query tokens
+// tok_lo .. tok_lo + ntok - 1 of the sequence (starting at q0), heads kvh*G .. kvh*G + G - 1.
+// Written at once, without the kernel's load pipeline.
+template <bool WT>
+__device__ __forceinline__ void write_empty_partials(const SplitArgs& a, int q0, int tok_lo, int ntok, int G, int kvh,
+                                                     int part, int dv, int nthreads) {
+  const int64_t Hq = a.num_q_heads, P = a.num_partitions;
+  const int rows = ntok * G, c4n = dv / 4;
+  for (int idx = threadIdx.x; idx < rows * c4n; idx += nthreads) {
+    const int r = idx / c4n, c4 = idx - r * c4n;
+    const int qi = r / G, hh = r - qi * G;
+    const int64_t rh = (int64_t)(q0 + tok_lo + qi) * Hq + kvh * G + hh;
+    store_partial4<WT>(a.part_out + (rh * P + part) * dv + c4 * 4, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+  for (int r = threadIdx.x; r < rows; r += nthreads) {
+    const int qi = r / G, hh = r - qi * G;
+    const int64_t rh = (int64_t)(q0 + tok_lo + qi) * Hq + kvh * G + hh;
+    store_partial1<WT>(a.part_lse + rh * P + part, -__builtin_inff());
+  }
+}
 
 bool splitkv_supported(const SplitArgs& a);
 bool launch_splitkv_partial(const SplitArgs& a, hipStream_t s);

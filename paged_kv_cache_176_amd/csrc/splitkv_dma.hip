@@ -88,6 +88,58 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
 
+  // ---- fused new-token write (decode): the workgroup whose key range holds key S-1
+  // (partition 0 when S == 0) owns token b's K/V row of this KV head.  DiffKV rows: its
+  // lanes load the row (chunk c of the row as it lies in the cache: lane c % 64) with Q,
+  // store it into the slot after the prologue's wait, and the wave that consumes the last
+  // tile copies it into that tile's LDS stage over whatever the DMA fetched for key S-1 (and
+  // for the keys past the partition, which re-read key S-1): the LDS then holds exactly
+  // what it would after a completed write, and no read waits on the store.  MLA rows, whose
+  // kernel has no registers to spare for the row: the owner writes it first and waits for
+  // the stores before any of its waves issues a read (its partition is the sequence's last
+  // and no longer than the others, so the wait is off the critical path) ----
+  constexpr bool kPatchRow = DK <= 256;
+  constexpr int RCH = (CH + 63) / 64;
+  constexpr int KCH = DK * ESZ / 16;             // chunks of the row that are K
+  const bool own = new_slot >= 0 && (S > 0 ? (start <= S - 1 && S - 1 < end) : part == 0);   // uniform
+  auto new_row_chunk = [&](int c) -> u32x4 {     // chunk c (16 bytes) of the new row, encoded
+    const bool isk = c < KCH;
+    const int e0 = (isk ? c : c - KCH) * (16 / ESZ);   // first element of the chunk
+    const uint16_t* src = isk ? a.ak + (int64_t)b * a.ak_st + (int64_t)kvh * a.ak_sh + e0
+                              : a.av + (int64_t)b * a.av_st + (int64_t)kvh * a.av_sh + e0;
+    if constexpr (FP8) {
+      const float* sp = isk ? a.c.k_scale : a.c.v_scale;
+      const float sc = a.c.scale_mode == 2 ? sp[kvh] : sp[0];
+      const u32x2 lo = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src), sc);
+      const u32x2 hi2 = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src + 8), sc);
+      return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+    } else {
+      return *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto new_row_base = [&]() -> uint8_t* {
+    const int64_t blk = new_slot / a.c.block_size;
+    return a.c.data + (blk * a.c.sb + (new_slot - blk * a.c.block_size) * a.c.ss + (int64_t)kvh * a.c.sh) * ESZ;
+  };
+
+  // ---- an empty key range (no key of the sequence here): empty partials at once, and the
+  // new row of a sequence without keys still goes to its slot ----
+  if (nt == 0) {                                 // workgroup-uniform
+    if (own && wave == 0) {
+      uint8_t* row = new_row_base();
+      for (int c = lane; c < CH; c += 64) *reinterpret_cast<u32x4*>(row + c * 16) = new_row_chunk(c);
+    }
+    write_empty_partials<(DK > 256)>(a, q0, 0, min(min(L, a.max_q), ROWS / G), G, kvh, part, DV, NW * 64);
+    return;
+  }
+
+  if (!kPatchRow && own) {                       // workgroup-uniform
+    uint8_t* row = new_row_base();
+    for (int c = threadIdx.x; c < CH; c += NW * 64) *reinterpret_cast<u32x4*>(row + c * 16) = new_row_chunk(c);
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): the row is in L2
+    __syncthreads();
+  }
+
   char* ring = smem + wave * WAVE_BYTES;
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * ESZ;
 
@@ -129,39 +181,13 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   for (int k = 0; k < NST; ++k)
     if (wave + k * NW < nt) issue(wave + k * NW, k);
 
-  // ---- fused new-token write (decode): the workgroup whose key range holds key S-1
-  // (partition 0 when S == 0) owns token b's K/V row of this KV head.  Its lanes load the
-  // row (chunk c of the row as it lies in the cache: lane c % 64), store it into the slot
-  // after the prologue's wait, and the wave that consumes the last tile copies it into
-  // that tile's LDS stage over whatever the DMA fetched for key S-1 (and for the keys past
-  // the partition, which re-read key S-1): the LDS then holds exactly what it would after
-  // a completed write, and no read waits on the store ----
-  constexpr int RCH = (CH + 63) / 64;
-  const bool own = new_slot >= 0 && (S > 0 ? (start <= S - 1 && S - 1 < end) : part == 0);   // uniform
-  u32x4 nrow[RCH];
+  u32x4 nrow[RCH];                               // the owner's new row, loaded with Q
 #pragma unroll
   for (int r = 0; r < RCH; ++r) nrow[r] = u32x4{0, 0, 0, 0};
-  if (own) {
-    constexpr int KCH = DK * ESZ / 16;           // chunks of the row that are K
+  if (kPatchRow && own) {
 #pragma unroll
-    for (int r = 0; r < RCH; ++r) {
-      const int c = lane + 64 * r;
-      if (c < CH) {
-        const bool isk = c < KCH;
-        const int e0 = (isk ? c : c - KCH) * (16 / ESZ);   // first element of the chunk
-        const uint16_t* src = isk ? a.ak + (int64_t)b * a.ak_st + (int64_t)kvh * a.ak_sh + e0
-                                  : a.av + (int64_t)b * a.av_st + (int64_t)kvh * a.av_sh + e0;
-        if constexpr (FP8) {
-          const float* sp = isk ? a.c.k_scale : a.c.v_scale;
-          const float sc = a.c.scale_mode == 2 ? sp[kvh] : sp[0];
-          const u32x2 lo = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src), sc);
-          const u32x2 hi2 = bf16x8_to_e4m3fn(*reinterpret_cast<const u32x4*>(src + 8), sc);
-          nrow[r] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
-        } else {
-          nrow[r] = *reinterpret_cast<const u32x4*>(src);
-        }
-      }
-    }
+    for (int r = 0; r < RCH; ++r)
+      if (lane + 64 * r < CH) nrow[r] = new_row_chunk(lane + 64 * r);
   }
 
   // ---- Q rows (B operand), visibility limits ----
@@ -198,16 +224,9 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     sl2 = -sl2;
   }
   // last key that every live row of this workgroup sees (tiles ending at or before it
-  // need no mask); rows past the query tokens never see any key and are ignored
-  int vis_hi = 0x7fffffff;
-#pragma unroll
-  for (int rg = 0; rg < NR; ++rg) {
-    const int qi = (rg * 16 + n) / G;
-    if (qi < L && qi < a.max_q) vis_hi = min(vis_hi, hi[rg]);
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) vis_hi = min(vis_hi, __shfl_xor(vis_hi, o, 64));
-  vis_hi = __builtin_amdgcn_readfirstlane(vis_hi);
+  // need no mask): the live rows' limits min(S - L + qi, end - 1) are smallest for token
+  // 0, whose rows are always here (row 0); rows past the query tokens see no key
+  const int vis_hi = min(L, a.max_q) > 0 ? min(S - L, end - 1) : 0x7fffffff;
 
   // lane byte offsets inside a tile: K operand chunk 4ks+g of key n (per ks parity; the
   // rest of ks is an immediate) and the transposed V source (per 16-dim block, mod 4)
@@ -243,22 +262,21 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   // count DMA instructions only, and the compiler, which counts only the loads it
   // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-  if (own && wave == 0) {                        // the new row into its cache slot
-    const int64_t blk = new_slot / a.c.block_size;
-    uint8_t* row = a.c.data + (blk * a.c.sb + (new_slot - blk * a.c.block_size) * a.c.ss + (int64_t)kvh * a.c.sh) * ESZ;
+  if (kPatchRow && own && wave == 0) {           // the new row into its cache slot
+    uint8_t* row = new_row_base();
 #pragma unroll
     for (int r = 0; r < RCH; ++r)
       if (lane + 64 * r < CH) *reinterpret_cast<u32x4*>(row + (lane + 64 * r) * 16) = nrow[r];
   }
   // the last tile's LDS rows from key S-1 on: the new row (see above)
-  auto patch_new_row = [&](int stage, int k) {
+  auto patch_new_row = [&](int stage, int k, const u32x4 (&row)[RCH]) {
     char* buf = ring + stage * TILE_BYTES;
     for (int kk = k; kk < TT; ++kk) {
       const int sw = FP8 ? sd_swz4(kk) : sd_swz(kk);
 #pragma unroll
       for (int r = 0; r < RCH; ++r) {
         const int c = lane + 64 * r;
-        if (c < CH) *reinterpret_cast<u32x4*>(buf + (kk * CH + (c ^ sw)) * 16) = nrow[r];
+        if (c < CH) *reinterpret_cast<u32x4*>(buf + (kk * CH + (c ^ sw)) * 16) = row[r];
       }
     }
   };
@@ -371,13 +389,14 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       const int tn = ti + (NST - 1) * NW;
       if (ti != wave && tn < nt) issue(tn, (stage + NST - 1) % NST);
       // tiles issued after ti: min(NST-1, remaining) -> wait until only those are in flight
+      const bool patch = kPatchRow && own && ti == nt - 1;   // wave-uniform: the owner's last tile
       const int later = min(NST - 1, (nt - 1 - ti) / NW);
       static_assert(NST <= 4, "waits below cover up to 3 tiles in flight");
       if (NST > 3 && later >= 3) wait_vm<(NST > 3 ? 3 : 0) * NINS>();
       else if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
       else if (later >= 1) wait_vm<NINS>();
       else wait_vm<0>();
-      if (own && ti == nt - 1) patch_new_row(stage, S - 1 - (start + ti * TT));   // wave-uniform
+      if (patch) patch_new_row(stage, S - 1 - (start + ti * TT), nrow);
       compute(ti, stage);
       stage = (stage + 1) % NST;
     }

@@ -82,6 +82,10 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, TT);
+  if (nt == 0) {                                 // an empty key range: empty partials at once
+    write_empty_partials<true>(a, q0, tg * NTOK, min(NTOK, Lq - tg * NTOK), G, kvh, part, DV, NW * 64);
+    return;
+  }
   const int nsteps = ceil_div(nt, 2);
   const int bs_shift = __builtin_ctz(a.c.block_size);
   const int bs_mask = a.c.block_size - 1;

@@ -80,6 +80,10 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int bs_shift = __builtin_ctz(a.c.block_size);
   const int bs_mask = a.c.block_size - 1;
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
+  if (nt == 0) {                                 // an empty key range: empty partials at once
+    write_empty_partials<true>(a, q0, 0, min(min(L, a.max_q), ROWS / G), G, kvh, part, DV, NW * 64);
+    return;
+  }
 
   // ---- per-lane LDS offsets ----
   // K: lane (m = n, g) reads chunk 2j + g of key pi(n); j even/odd differ in bit 1 of
@@ -179,10 +183,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   // normal scale gives the same uniform weights to within fp32 rounding
   sl2 = fmaxf(sl2, 1.17549435e-38f);
   // last key every live row sees: tiles ending at or before it need no mask
-  int vis_hi = live ? hi : 0x7fffffff;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) vis_hi = min(vis_hi, __shfl_xor(vis_hi, o, 64));
-  vis_hi = __builtin_amdgcn_readfirstlane(vis_hi);
+  // (the live rows' limits min(S - L + qi, end - 1) are smallest for token 0, whose rows
+  // are always here)
+  const int vis_hi = min(L, a.max_q) > 0 ? min(S - L, end - 1) : 0x7fffffff;
 
   f32x16 acc[DBW];
 #pragma unroll
