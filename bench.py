@@ -41,7 +41,7 @@ MALL_BYTES = 256 << 20
 MEASURED_TRAFFIC = {
     ("6ad4e3342588c612", 128): 164007.6 * 1024 * 2 + 2178.7 * 1024,
 }
-KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp")
+KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp", "kernels.hpp")
 
 
 def _kernel_source_hash():
@@ -497,10 +497,23 @@ def run_decode_extra(b, s, bs, steps, warmup, cpu=True):
     return decode_line(c, f"decode_b{b}_s{s}_bs{bs}", steps, warmup, cpu)
 
 
-# context buckets -> active splits for the mixed decode batch (4 KV heads, two 4-wave
-# workgroups per CU): about 512 keys per split, at most 64
-MIXED_POLICY = [(2048, 4), (8192, 16), (32768, 32), (1 << 30, 64)]
 MIXED_LENS = [131072, 65536, 16384, 8192, 4096, 2048, 1024, 256]
+# context buckets -> active splits for the mixed decode batch (launch P 64), chosen by the
+# measured sweep below (`--only policy_sweep`): the candidates that cut the splits of the
+# mid-length sequences further, or that let the long ones take more than 64, all measured
+# slower than a plain 64 (every inactive workgroup still costs a dispatch and a prologue);
+# halving the splits of sequences up to 4096 keys ties or beats it
+MIXED_POLICY = [(4096, 32), (1 << 30, 64)]
+POLICY_CANDIDATES = [
+    ("fixed64", 64, None),
+    ("short32", 64, MIXED_POLICY),
+    ("short16", 64, [(1024, 16), (1 << 30, 64)]),
+    ("tail8", 64, [(256, 8), (2048, 32), (1 << 30, 64)]),
+    ("512keys", 64, [(2048, 4), (8192, 16), (32768, 32), (1 << 30, 64)]),
+    ("long96", 96, [(32768, 64), (1 << 30, 96)]),
+    ("geo1024", 128, [(1024, 1), (2048, 2), (4096, 4), (8192, 8), (16384, 16), (32768, 32), (65536, 64),
+                      (1 << 30, 128)]),
+]
 
 
 def run_decode_mixed(steps, warmup, cpu=True):
@@ -523,6 +536,24 @@ def run_decode_mixed(steps, warmup, cpu=True):
     if cpu:
         defer_cpu(res, lambda: oracle_seconds(w, 2.0, with_write=True), algo, "GB/s",
                   "a whole decode step of the 8 sequences (cache write + fp64 attention)")
+    return res
+
+
+def run_policy_sweep(steps, warmup):
+    """The split-policy candidates on the mixed batch, each timed twice (event-free steps)."""
+    import torch
+    import workloads
+    w = workloads.paged_workload("decode_mixed", workloads.diffkv_geom(0, 16), MIXED_LENS, [1] * len(MIXED_LENS), 32,
+                                 1.0 / math.sqrt(192), seed=0, write_all=False)
+    res = {"workload": "decode_mixed_b8_bs16", "lens": MIXED_LENS, "us_per_step": {}}
+    for rep in range(2):
+        for name, P, pol in POLICY_CANDIDATES:
+            c = DecodeCase(w, P, policy=pol)
+            d, _, _ = time_steps(c.step, steps, warmup)
+            res["us_per_step"].setdefault(name, []).append(round(d * 1e6, 2))
+            del c
+            torch.cuda.empty_cache()
+    res["policies"] = {name: {"P": P, "policy": pol} for name, P, pol in POLICY_CANDIDATES}
     return res
 
 
@@ -619,6 +650,8 @@ def run_only(name, steps, warmup):
         return run_decode_mixed(steps, warmup, cpu=False)
     if name == "copy":
         return copy_rate()
+    if name == "policy_sweep":
+        return run_policy_sweep(steps, warmup)
     return run_decode_extra(8, 8192, 16, steps, warmup, cpu=False)
 
 
@@ -635,7 +668,7 @@ def main():
     ap.add_argument("--spinup-ms", type=float, default=SPINUP_MS,
                     help="untimed running of each measured step before its warmup steps (GPU clock spin-up)")
     ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "mla_verify_b1", "mla_verify_b16",
-                             "decode_mixed", "decode_b8", "copy"], default=None,
+                             "decode_mixed", "decode_b8", "copy", "policy_sweep"], default=None,
                     help="run just this secondary workload and print its JSON line (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
