@@ -670,6 +670,9 @@ def main():
     ap.add_argument("--only", choices=["prefill", "fp8_verify", "mla_b1", "mla_b16", "mla_verify_b1", "mla_verify_b16",
                              "decode_mixed", "decode_b8", "copy", "policy_sweep"], default=None,
                     help="run just this secondary workload and print its JSON line (for profiling)")
+    ap.add_argument("--phase-stamps", choices=sorted(STAMP_CASES), default=None,
+                    help="load the library built with the decode kernel's phase stamps and print the per-wave "
+                         "timeline of this decode workload (diagnostics; no timing line)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
                          "size that calibrates hardware byte counters)")
@@ -683,6 +686,12 @@ def main():
     import torch
     import paged_kv_cache_176_amd as pk
     import workloads
+    if args.phase_stamps:
+        from paged_kv_cache_176_amd import build as pkb
+        pk.ops.use_library(pkb.STAMPS_LIB)
+        assert torch.cuda.is_available(), "bench.py needs the GPU"
+        print(json.dumps(phase_stamps(args.phase_stamps)), flush=True)
+        return
     pk.load_library()
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.only:
@@ -778,6 +787,60 @@ def main():
     if args.copy_probe_mib:
         line["copy_probe_bytes"] = copy_probe(args.copy_probe_mib)
     print(json.dumps(line), flush=True)
+
+
+STAMP_CASES = {   # name -> (workload, KV heads, the launch's split count)
+    "decode_b1": (lambda w: w.long_decode(1, 131072, 16), 4, lambda: auto_partitions(1, 4, 131072, wgs_per_cu=2)),
+    "decode_b8": (lambda w: w.long_decode(8, 8192, 16), 4, lambda: auto_partitions(8, 4, 8192, wgs_per_cu=2)),
+    "mla_b1": (lambda w: w.mla_decode(1, 100000), 1, lambda: auto_partitions(1, 1, 100000)),
+    "mla_b16": (lambda w: w.mla_decode(16, 100000), 1, lambda: auto_partitions(16, 1, 100000)),
+}
+
+
+def phase_stamps(name, launches=40):
+    """Per-wave phase timeline of the decode partial kernel, from the library built with its
+    phase stamps (the last of `launches` back-to-back launches of the partial kernel):
+    percentiles over all waves of each phase's time from the first wave's entry, of the
+    per-tile wait and compute, and the end time per XCC."""
+    import ctypes
+    import numpy as np
+    import torch
+    import paged_kv_cache_176_amd as pk
+    import workloads
+    lib = pk.load_library()
+    lib.attn_phase_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    make, hkv, parts = STAMP_CASES[name]
+    w = make(workloads)
+    P = parts()
+    c = DecodeCase(w, P)
+    for i in range(launches):
+        c.partial(i)
+    torch.cuda.synchronize()
+    waves = P * hkv * int(w.seq_lens.numel()) * 4
+    buf = np.zeros(waves * 64, dtype=np.uint32)
+    rc = lib.attn_phase_stamps_read(buf.ctypes.data, buf.size)
+    if rc != 0:
+        raise RuntimeError(f"attn_phase_stamps_read failed ({rc})")
+    st = buf.reshape(waves, 64).astype(np.int64)
+    rel = (st - st[:, 0].min()) * 0.01                 # s_memrealtime ticks at 100 MHz -> us
+    q = lambda a: {k: round(float(np.percentile(a, v)), 2) for k, v in (("min", 0), ("p10", 10), ("p50", 50),
+                                                                         ("p90", 90), ("max", 100))}
+    ntiles = st[:, 58]
+    res = {"workload": name, "partitions": P, "waves": waves, "tiles_per_wave": sorted(set(ntiles.tolist())),
+           "us_from_first_entry": {"entry": q(rel[:, 0]), "prologue_issued": q(rel[:, 1]),
+                                   "first_tiles_landed": q(rel[:, 2]), "loop_end": q(rel[:, 60]),
+                                   "epilogue_barrier": q(rel[:, 61]), "end": q(rel[:, 62])}}
+    tiles = []
+    for k in range(min(int(ntiles.max()), 27)):       # over the waves that consume a k-th tile
+        r = rel[ntiles > k]
+        wait = r[:, 3 + 2 * k] - (r[:, 2] if k == 0 else r[:, 4 + 2 * (k - 1)])
+        tiles.append({"tile": k, "waves": int(len(r)), "wait_us": q(wait),
+                      "compute_us": q(r[:, 4 + 2 * k] - r[:, 3 + 2 * k])})
+    res["tiles"] = tiles
+    xcc = st[:, 59] & 0xF
+    res["end_us_by_xcc"] = {int(x): q(rel[xcc == x, 62]) for x in np.unique(xcc)}
+    res["corr_first_tiles_vs_loop_end"] = round(float(np.corrcoef(rel[:, 2], rel[:, 60])[0, 1]), 3)
+    return res
 
 
 def copy_probe(mib):

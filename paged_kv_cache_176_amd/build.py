@@ -15,6 +15,10 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
+# the same library with the decode kernel's per-wave phase stamps compiled in (diagnostics
+# only: bench.py --phase-stamps loads it; the entry points' library never carries them)
+STAMPS_LIB = os.path.join(HERE, "libpagedattn_stamps.so")
+STAMPED_SOURCE = "splitkv_dma.hip"
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip",
            "prefill.hip"]
@@ -34,9 +38,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, extra=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + tag + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -46,19 +50,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library (and its phase-stamped twin);
+    returns the library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(src, (), "") for src in SOURCES] + [(STAMPED_SOURCE, ("-DPA_PHASE_STAMPS",), ".stamps")]
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    stamped = [objs[-1] if src == STAMPED_SOURCE else o for src, o in zip(SOURCES, objs)]
+    _link(stamped, STAMPS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {os.path.basename(STAMPS_LIB)}")
     return LIB
 
 

@@ -27,6 +27,49 @@
 #include "kernels.hpp"
 
 namespace pa {
+
+// ---- phase stamps: an instrumented build only (compiled with -DPA_PHASE_STAMPS into
+// libpagedattn_stamps.so; the library the entry points ship in has none of this).  Every
+// wave keeps up to 64 s_memrealtime readings (100 MHz) in one register, lane k holding
+// stamp k, and stores them at its end to g_phase_stamps[(workgroup * 4 + wave) * 64 + k]
+// (workgroup = (z * gridDim.y + y) * gridDim.x + x; waves past kStampWaves are not kept):
+//   0 entry, 1 ring prologue issued, 2 Q and the first tiles landed, 3 + 2i / 4 + 2i the
+//   wave's i-th tile after its wait / after its compute (i < 27; later tiles overwrite the
+//   27th), 58 tiles consumed, 59 XCC id, 60 loop end, 61 first epilogue barrier passed,
+//   62 end, 63 HW_ID ----
+#ifdef PA_PHASE_STAMPS
+constexpr int kStampWaves = 1 << 14;
+__device__ uint32_t g_phase_stamps[kStampWaves * 64];
+#define PA_STAMP_DECL uint32_t st_ = 0; int it_ = 0;
+#define PA_STAMP(k)                                                            \
+  {                                                                            \
+    const uint32_t t_ = (uint32_t)__builtin_amdgcn_s_memrealtime();            \
+    st_ = lane == (k) ? t_ : st_;                                              \
+  }
+#define PA_STAMP_TILE_WAITED PA_STAMP(3 + 2 * it_)
+#define PA_STAMP_TILE_DONE                                                     \
+  {                                                                            \
+    PA_STAMP(4 + 2 * it_);                                                     \
+    it_ = it_ < 27 ? it_ + 1 : it_;                                            \
+  }
+#define PA_STAMP_FLUSH                                                         \
+  {                                                                            \
+    PA_STAMP(62);                                                              \
+    const uint32_t hw_ = __builtin_amdgcn_s_getreg((31 << 11) | 4);           \
+    const uint32_t xcc_ = __builtin_amdgcn_s_getreg((31 << 11) | 20);         \
+    st_ = lane == 63 ? hw_ : lane == 59 ? xcc_ : lane == 58 ? (uint32_t)it_ : st_; \
+    const int64_t wg_ = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x; \
+    const int64_t w_ = wg_ * sd::NW + wave;                                    \
+    if (w_ < kStampWaves) g_phase_stamps[w_ * 64 + lane] = st_;                \
+  }
+#else
+#define PA_STAMP_DECL
+#define PA_STAMP(k)
+#define PA_STAMP_TILE_WAITED
+#define PA_STAMP_TILE_DONE
+#define PA_STAMP_FLUSH
+#endif
+
 namespace sd {
 constexpr int NW = 4;
 constexpr int TT = 16;                 // keys per tile
@@ -71,6 +114,8 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   const int n = lane & 15, g = lane >> 4;
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
+  PA_STAMP_DECL
+  PA_STAMP(0)
   // every per-sequence scalar in one round trip (NULL arguments read zeros): the block ids
   // of the first tiles wait on seq_len, and nothing else should sit in front of them
   const int32_t* qslp = a.qsl ? a.qsl + b : reinterpret_cast<const int32_t*>(kZeroScalars);
@@ -130,6 +175,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       for (int c = lane; c < CH; c += 64) *reinterpret_cast<u32x4*>(row + c * 16) = new_row_chunk(c);
     }
     write_empty_partials<(DK > 256)>(a, q0, 0, min(min(L, a.max_q), ROWS / G), G, kvh, part, DV, NW * 64);
+    PA_STAMP_FLUSH
     return;
   }
 
@@ -190,6 +236,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       if (lane + 64 * r < CH) nrow[r] = new_row_chunk(lane + 64 * r);
   }
 
+  PA_STAMP(1)
   // ---- Q rows (B operand), visibility limits ----
   bf16x8 qreg[NR][KS];
   int hi[NR];
@@ -262,6 +309,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   // count DMA instructions only, and the compiler, which counts only the loads it
   // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
+  PA_STAMP(2)
   if (kPatchRow && own && wave == 0) {           // the new row into its cache slot
     uint8_t* row = new_row_base();
 #pragma unroll
@@ -396,8 +444,10 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       else if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
       else if (later >= 1) wait_vm<NINS>();
       else wait_vm<0>();
+      PA_STAMP_TILE_WAITED
       if (patch) patch_new_row(stage, S - 1 - (start + ti * TT), nrow);
       compute(ti, stage);
+      PA_STAMP_TILE_DONE
       stage = (stage + 1) % NST;
     }
   }
@@ -405,9 +455,11 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   // ---- merge the NW waves: each writes its scaled accumulator to its own LDS slab
   // (independent stores, no read-modify-write chain), then all threads sum the slabs
   // in wave order and write the partials of the live rows ----
+  PA_STAMP(60)
 #pragma unroll
   for (int rg = 0; rg < NR; ++rg) l[rg] = sum_over_groups(l[rg]);
   __syncthreads();                                // rings are dead from here on
+  PA_STAMP(61)
   float* mw = reinterpret_cast<float*>(smem);     // [NW][ROWS]
   float* lw = mw + NW * ROWS;                     // [NW][ROWS]
   float* slab = lw + NW * ROWS;                   // [NW][ROWS][MERGE_PITCH]
@@ -460,6 +512,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
                      (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2);
     }
   }
+  PA_STAMP_FLUSH
 }
 
 // Eligible shapes: DiffKV rows, bf16 or fp8 (up to 32 rows per KV head), and bf16 MLA
@@ -502,3 +555,12 @@ void launch_splitkv_dma(const SplitArgs& a, hipStream_t s) {
 }
 
 }  // namespace pa
+
+#ifdef PA_PHASE_STAMPS
+// Copies the first `words` stamp words (at most kStampWaves * 64) to host memory `dst`;
+// returns the hipError_t of the copy.
+extern "C" int attn_phase_stamps_read(void* dst, size_t words) {
+  if (!dst || words > (size_t)pa::kStampWaves * 64) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(pa::g_phase_stamps), words * 4, 0, hipMemcpyDeviceToHost);
+}
+#endif

@@ -52,6 +52,16 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def use_library(path: str):
+    """Make `path` (a build of the same sources, e.g. the phase-stamped diagnostics library)
+    the library every entry point calls; must precede the first call."""
+    global _LIB_PATH, _lib
+    if _lib is not None:
+        raise RuntimeError("use_library: a library is already loaded")
+    _LIB_PATH = path
+    return load_library()
+
+
 def load_library(path: Optional[str] = None):
     """Load the HIP library; raises if it has not been built."""
     global _lib

@@ -1,0 +1,32 @@
+"""The phase-stamped diagnostics build of the decode kernel runs and gives a consistent
+per-wave timeline (bench.py --phase-stamps, in a process of its own since it loads the
+stamped twin of the library)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+# tiles per wave: B8 512 keys per partition / 16-key tiles / 4 waves; MLA B1 448 keys per
+# partition (7 per wave), the last partition 100000 - 223 x 448 = 96 keys (2, 2, 1, 1)
+@pytest.mark.parametrize("name,tiles", [("decode_b8", [8]), ("mla_b1", [1, 2, 7])])
+def test_phase_timeline(name, tiles):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--phase-stamps", name],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    res = json.loads([x for x in r.stdout.splitlines() if x.startswith("{")][-1])
+    assert res["tiles_per_wave"] == tiles
+    ph = res["us_from_first_entry"]
+    order = ["entry", "prologue_issued", "first_tiles_landed", "loop_end", "epilogue_barrier", "end"]
+    for a, b in zip(order, order[1:]):
+        assert ph[a]["min"] <= ph[b]["min"] and ph[a]["max"] <= ph[b]["max"], (a, b, ph[a], ph[b])
+    assert 0 < ph["end"]["max"] < 1000                 # one launch, in microseconds
+    assert len(res["tiles"]) == max(tiles)
+    assert res["tiles"][0]["waves"] == res["waves"]
+    assert all(t["compute_us"]["min"] >= 0 and t["wait_us"]["min"] >= 0 for t in res["tiles"])
+    assert len(res["end_us_by_xcc"]) == 8
