@@ -325,11 +325,16 @@ static_assert(SLOTS % (64 * NW) == 0, "stage must split evenly over the waves");
 }  // namespace pf
 
 // K chunk swizzle: a permutation over any 8 consecutive keys and distinct in (key parity,
-// swizzle) over 16 keys, so 16-byte operand reads are conflict-free whether the LDS serves
-// 8 lanes over 32 banks or 16 lanes over 64 banks per cycle.  Depends on key bits 0-3 only.
+// swizzle) over 16 keys; the 16-byte K-operand reads of 32 keys measure conflict-free with
+// it (LDS bank-conflict counter).  Depends on key bits 0-3 only.
 __device__ __forceinline__ int pf_k_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
 __device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ pf_k_swz(key)); }
-__device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ ((key & 7) << 1)); }
+// V rows are 256 bytes (all 64 banks of 4 bytes): the transposing V^T read, served 32
+// lanes at a time, puts 4 keys x 64 bytes (32 dims per key) on those lanes; XOR-ing the chunk index with (key & 3) << 2 gives the 4 keys 4 different
+// 64-byte quarters of the bank space (conflict-free on the counter, where the previous
+// (key & 7) << 1 left 2-way conflicts)
+__device__ __forceinline__ int pf_v_swz(int key) { return (key & 3) << 2; }
+__device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ pf_v_swz(key)); }
 
 #define PF_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 __device__ __forceinline__ void pf_barrier() {
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     } else {
       const int vs = slot - KSLOTS;
       dkey[u] = vs / VCH;
-      dbyte[u] = VOFF * 2 + ((vs - dkey[u] * VCH) ^ ((dkey[u] & 7) << 1)) * 16;
+      dbyte[u] = VOFF * 2 + ((vs - dkey[u] * VCH) ^ pf_v_swz(dkey[u])) * 16;
     }
   }
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * 2;

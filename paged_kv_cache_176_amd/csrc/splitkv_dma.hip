@@ -75,13 +75,19 @@ constexpr int NW = 4;
 constexpr int TT = 16;                 // keys per tile
 }  // namespace sd
 
-// chunk swizzles (XOR on a row's 16-byte chunk index) that keep 16 lanes reading
-// 16 different rows conflict-free.  640- and 1152-byte rows (bf16): as in the prefill
-// kernel, within groups of 8 chunks.  320-byte rows (fp8): a row pitch of 20 chunks
-// leaves only 4 distinct bank offsets per 4 rows, so chunks are permuted within
-// groups of 4 by ((key >> 2) ^ (key >> 1)) & 3, distinct for the 4 keys of one
-// offset class and for the 4 keys of one parity in every 8-key half.
-__device__ __forceinline__ int sd_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
+// chunk swizzles (XOR on a row's 16-byte chunk index).  640- and 1152-byte rows (bf16),
+// within groups of 8 chunks: key & 6.  The LDS has 64 banks of 4 bytes and serves a
+// 64-bit read 32 lanes at a time; the transposing V^T read puts 8 keys on those 32 lanes
+// (4 lanes, 32 bytes, per key), and since both row pitches are 128 bytes mod 256, odd
+// keys sit 128 bytes past even ones: XOR-ing with key & 6 gives keys 0, 2, 4, 6 (and 1, 3,
+// 5, 7) four different 32-byte chunk pairs, so the 32 lanes cover the 64 banks once.  The
+// 16-byte K-operand reads of 16 consecutive keys are conflict-free with it as well (both
+// measured with the LDS bank-conflict counter; the previous ((key >> 1) ^ (key << 2)) & 7
+// left the V^T reads 2-way conflicted).  320-byte rows (fp8): a row pitch of 20 chunks
+// leaves only 4 distinct bank offsets per 4 rows, so chunks are permuted within groups of
+// 4 by ((key >> 2) ^ (key >> 1)) & 3, distinct for the 4 keys of one offset class and for
+// the 4 keys of one parity in every 8-key half.
+__device__ __forceinline__ int sd_swz(int key) { return key & 6; }
 __device__ __forceinline__ int sd_swz4(int key) { return ((key >> 2) ^ (key >> 1)) & 3; }
 
 // FP8: E4M3FN rows; K chunks are converted to bf16 at the MFMA, V chunks are converted
@@ -363,6 +369,23 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
           for (int rg = 0; rg < NR; ++rg)
             s[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[rg][2 * j + h], s[rg], 0, 0, 0);
         }
+      }
+    } else if constexpr (DK > 256) {
+      // MLA rows: 18 dependent k-steps on one wave per SIMD.  The K operands are read KPF
+      // k-steps ahead of their MFMAs, and a scheduling barrier after each k-step keeps that
+      // order (left to itself the compiler reads each operand right before its MFMA, and
+      // the chain waits on every LDS read)
+      static_assert(NR == 1, "MLA rows: one row group");
+      constexpr int KPF = 3;
+      bf16x8 kb[KPF + 1];
+#pragma unroll
+      for (int j = 0; j < KPF; ++j) kb[j] = *reinterpret_cast<const bf16x8*>(buf + koff[j & 1] + (j >> 1) * 128);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int jn = ks + KPF;
+        if (jn < KS) kb[jn % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(buf + koff[jn & 1] + (jn >> 1) * 128);
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks % (KPF + 1)], qreg[0][ks], s[0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll

@@ -43,10 +43,14 @@ constexpr int NST = 4;                 // ring stages (two steps of two tiles)
 constexpr int DK = 576, DV = 512;      // latent row; V = its first DV columns
 }  // namespace stk
 
-// XOR swizzle of a row's 16-byte chunk index within groups of 8 chunks: 16 lanes reading
-// 16 consecutive rows of 1152 bytes hit 16 different bank groups.  It depends on the row
-// mod 16 only, so both 16-key halves of a tile share it.
-__device__ __forceinline__ int tok_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
+// XOR swizzle of a row's 16-byte chunk index within groups of 8 chunks: key & 6.  Rows of
+// 1152 bytes put odd keys 128 bytes (mod 256) past even ones, and the LDS (64 banks of 4
+// bytes) serves a 64-bit read 32 lanes at a time: the transposing V^T read's 8 keys per 32
+// lanes then take four different 32-byte chunk pairs per key parity, covering the 64
+// banks once, and the 16-byte K reads of 16 consecutive keys stay conflict-free (both
+// measured with the LDS bank-conflict counter).  It depends on the row mod 16 only, so
+// both 16-key halves of a tile share it.
+__device__ __forceinline__ int tok_swz(int key) { return key & 6; }
 
 __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitArgs a) {
   using namespace stk;
@@ -107,10 +111,15 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     const int r0 = min(16 * (tw >> 1), kmax);
     const int64_t blk = load_uniform(btrow + ((t0 + r0) >> bs_shift));
     const uint8_t* base = head_base + (blk * a.c.sb + (int64_t)((t0 + r0) & bs_mask) * a.c.ss) * 2;
+    // the lane index passes through an empty asm so that the share's offsets are computed
+    // here, at each issue, instead of being hoisted and held in registers for the whole
+    // loop (which spilled, and left the QK^T loop no registers to read ahead)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < SHARE; ++i) {
       const int u = tw * SHARE + i;
-      const int slot = u * 64 + lane;
+      const int slot = u * 64 + ln;
       const int key = slot / CH;
       const int c = (slot - key * CH) ^ tok_swz(key);
       dma16_nt_s((uint32_t)((min(key, kmax) - r0) * ssb + c * 16), base, lds_addr(buf + u * 1024));
@@ -170,12 +179,26 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     const char* buf = ring + (k & (NST - 1)) * TILE_BYTES;
     const int j0 = start + k * TT;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // the K operands are read KPF k-steps ahead of their MFMAs, and a scheduling barrier
+    // after each k-step keeps that order (left to itself the compiler reads each operand
+    // right before its MFMA, and the two dependent chains wait on every LDS read)
+    constexpr int KPF = 2;
+    bf16x8 kb0[KPF + 1], kb1[KPF + 1];
+#pragma unroll
+    for (int j = 0; j < KPF; ++j) {
+      kb0[j] = *reinterpret_cast<const bf16x8*>(buf + koff[j & 1] + (j >> 1) * 128);
+      kb1[j] = *reinterpret_cast<const bf16x8*>(buf + HALF + koff[j & 1] + (j >> 1) * 128);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(buf + koff[ks & 1] + (ks >> 1) * 128);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(buf + HALF + koff[ks & 1] + (ks >> 1) * 128);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[ks], s1, 0, 0, 0);
+      const int jn = ks + KPF;
+      if (jn < KS) {
+        kb0[jn % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(buf + koff[jn & 1] + (jn >> 1) * 128);
+        kb1[jn % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(buf + HALF + koff[jn & 1] + (jn >> 1) * 128);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0[ks % (KPF + 1)], qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1[ks % (KPF + 1)], qreg[ks], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (kn >= 0) issue(kn);
     // lane (n, g): keys j0 + 4g + i (s0) and j0 + 16 + 4g + i (s1) of row n.  A tile the
