@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("7835307391fbb192", 128): 164006.5 * 1024 * 2 + 2178.6 * 1024,
+    ("3aa3550959003f8d", 128): 164006.6 * 1024 * 2 + 2178.7 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp", "kernels.hpp")
 

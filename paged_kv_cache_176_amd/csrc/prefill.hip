@@ -567,6 +567,25 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], s, 0, 0, 0);
     }
   };
+  // the same QK^T with its K operands read four k-steps ahead, the order held by a
+  // scheduling barrier after each k-step: the block that runs at raised priority, where
+  // the compiler's own order read each operand right before its MFMA and waited for it
+  auto qk_half_ahead = [&](const char* buf, int h, f32x16& s) {
+    constexpr int KPF = 4;
+    const char* kbuf = buf + h * (32 * KCH * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    bf16x8 kb[KPF + 1];
+#pragma unroll
+    for (int j = 0; j < KPF; ++j) kb[j] = *reinterpret_cast<const bf16x8*>(kbuf + koff[j & 3] + (j >> 2) * 128);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int jn = ks + KPF;
+      if (jn < KS) kb[jn % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(kbuf + koff[jn & 3] + (jn >> 2) * 128);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[ks % (KPF + 1)], qreg[ks], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // softmax of one unmasked half: updates m and l, returns P as bf16 and the factor the
   // accumulator must be scaled by before this half's PV (1 unless the max grew)
   auto softmax_half = [&](f32x16& s, uint32_t (&pk)[8]) -> float {
@@ -616,7 +635,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     // matrix core's gaps (chunked prefill 1.3% faster; the same schedule without the
     // priority is 2% slower, and raising it over region 1 as well, 2-3% slower).
     __builtin_amdgcn_s_setprio(1);
-    qk_half(buf, 0, s0);
+    qk_half_ahead(buf, 0, s0);
     __builtin_amdgcn_s_setprio(0);
     // region 1: QK of the second half while the first half's softmax runs: 12 K-operand
     // reads running three MFMAs ahead (a read issued just before its MFMA exposes a whole
