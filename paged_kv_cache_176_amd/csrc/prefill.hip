@@ -20,6 +20,7 @@
 //   order:     heaviest query tiles first (they see the most keys).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_layout.hpp"
 
 namespace pa {
 
@@ -324,17 +325,10 @@ constexpr int DB = DV / 32;              // 4 output dim blocks
 static_assert(SLOTS % (64 * NW) == 0, "stage must split evenly over the waves");
 }  // namespace pf
 
-// K chunk swizzle: a permutation over any 8 consecutive keys and distinct in (key parity,
-// swizzle) over 16 keys; the 16-byte K-operand reads of 32 keys measure conflict-free with
-// it (LDS bank-conflict counter).  Depends on key bits 0-3 only.
-__device__ __forceinline__ int pf_k_swz(int key) { return ((key >> 1) ^ (key << 2)) & 7; }
-__device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ pf_k_swz(key)); }
-// V rows are 256 bytes (all 64 banks of 4 bytes): the transposing V^T read, served 32
-// lanes at a time, puts 4 keys x 64 bytes (32 dims per key) on those lanes; XOR-ing the chunk index with (key & 3) << 2 gives the 4 keys 4 different
-// 64-byte quarters of the bank space (conflict-free on the counter, where the previous
-// (key & 7) << 1 left 2-way conflicts)
-__device__ __forceinline__ int pf_v_swz(int key) { return (key & 3) << 2; }
-__device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ pf_v_swz(key)); }
+// chunk swizzles of the stage rows: lds_layout.hpp (prefill_k_swz for the 384-byte K rows,
+// prefill_v_swz for the 256-byte V rows)
+__device__ __forceinline__ int pf_k_slot(int key, int c) { return key * pf::KCH + (c ^ prefill_k_swz(key)); }
+__device__ __forceinline__ int pf_v_slot(int key, int c) { return pf::KSLOTS + key * pf::VCH + (c ^ prefill_v_swz(key)); }
 
 #define PF_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 __device__ __forceinline__ void pf_barrier() {
@@ -410,11 +404,11 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
     const int slot = (wave * PER_WAVE + u) * 64 + lane;
     if (slot < KSLOTS) {
       dkey[u] = slot / KCH;
-      dbyte[u] = ((slot - dkey[u] * KCH) ^ pf_k_swz(dkey[u])) * 16;
+      dbyte[u] = ((slot - dkey[u] * KCH) ^ prefill_k_swz(dkey[u])) * 16;
     } else {
       const int vs = slot - KSLOTS;
       dkey[u] = vs / VCH;
-      dbyte[u] = VOFF * 2 + ((vs - dkey[u] * VCH) ^ pf_v_swz(dkey[u])) * 16;
+      dbyte[u] = VOFF * 2 + ((vs - dkey[u] * VCH) ^ prefill_v_swz(dkey[u])) * 16;
     }
   }
   const uint8_t* head_base = a.c.data + (int64_t)kvh * a.c.sh * 2;
@@ -422,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fast_kernel(PrefillArgs a, int
   // reads (per 32-dim block), relative to the stage buffer
   int koff[4], voff[DB];
   {
-    const int sw = pf_k_swz(n32);                 // = pf_k_swz(32h + n32) for both halves
+    const int sw = prefill_k_swz(n32);                 // = prefill_k_swz(32h + n32) for both halves
 #pragma unroll
     for (int r = 0; r < 4; ++r) koff[r] = (n32 * KCH + ((2 * r + g) ^ sw)) * 16;
     const int s16 = lane & 15, half = (lane >> 4) & 1;

@@ -25,6 +25,7 @@
 // The waves' (m, l, acc) merge through LDS in a fixed order at the end.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_layout.hpp"
 
 namespace pa {
 
@@ -75,20 +76,8 @@ constexpr int NW = 4;
 constexpr int TT = 16;                 // keys per tile
 }  // namespace sd
 
-// chunk swizzles (XOR on a row's 16-byte chunk index).  640- and 1152-byte rows (bf16),
-// within groups of 8 chunks: key & 6.  The LDS has 64 banks of 4 bytes and serves a
-// 64-bit read 32 lanes at a time; the transposing V^T read puts 8 keys on those 32 lanes
-// (4 lanes, 32 bytes, per key), and since both row pitches are 128 bytes mod 256, odd
-// keys sit 128 bytes past even ones: XOR-ing with key & 6 gives keys 0, 2, 4, 6 (and 1, 3,
-// 5, 7) four different 32-byte chunk pairs, so the 32 lanes cover the 64 banks once.  The
-// 16-byte K-operand reads of 16 consecutive keys are conflict-free with it as well (both
-// measured with the LDS bank-conflict counter; the previous ((key >> 1) ^ (key << 2)) & 7
-// left the V^T reads 2-way conflicted).  320-byte rows (fp8): a row pitch of 20 chunks
-// leaves only 4 distinct bank offsets per 4 rows, so chunks are permuted within groups of
-// 4 by ((key >> 2) ^ (key >> 1)) & 3, distinct for the 4 keys of one offset class and for
-// the 4 keys of one parity in every 8-key half.
-__device__ __forceinline__ int sd_swz(int key) { return key & 6; }
-__device__ __forceinline__ int sd_swz4(int key) { return ((key >> 2) ^ (key >> 1)) & 3; }
+// chunk swizzles of the ring rows: lds_layout.hpp (bf16 rows row_chunk_swz, fp8 rows
+// fp8_chunk_swz)
 
 // FP8: E4M3FN rows; K chunks are converted to bf16 at the MFMA, V chunks are converted
 // into a per-wave bf16 [key][dim] tile for the transposing read.  NTL: nontemporal DMA.
@@ -201,7 +190,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   auto dma_off = [&](int u, int kmax) {
     const int slot = u * 64 + lane;
     const int key = slot / CH;
-    const int c = (slot - key * CH) ^ (FP8 ? sd_swz4(key) : sd_swz(key));
+    const int c = (slot - key * CH) ^ (FP8 ? fp8_chunk_swz(key) : row_chunk_swz(key));
     return min(key, kmax) * ssb + c * 16;
   };
   constexpr bool kKeepOff = NINS <= 10;          // precomputed offsets (MLA rows: registers are full)
@@ -283,7 +272,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 
   // lane byte offsets inside a tile: K operand chunk 4ks+g of key n (per ks parity; the
   // rest of ks is an immediate) and the transposed V source (per 16-dim block, mod 4)
-  const int sw = FP8 ? sd_swz4(n) : sd_swz(n);
+  const int sw = FP8 ? fp8_chunk_swz(n) : row_chunk_swz(n);
   int koff[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) koff[par] = (n * CH + ((4 * par + g) ^ sw)) * 16;
@@ -294,7 +283,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     for (int d4 = 0; d4 < 4; ++d4) voff[d4] = ((4 * g + (n >> 2)) * VP + 16 * d4 + 4 * (n & 3)) * 2;
   } else {
     const int vkey = 4 * g + (n >> 2);
-    const int vsw = sd_swz(vkey);
+    const int vsw = row_chunk_swz(vkey);
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
       const int ch = VOFF / 8 + 2 * d4 + ((n & 3) >> 1);   // chunk of dims 16*d4 + 4*(n&3)
@@ -326,7 +315,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
   auto patch_new_row = [&](int stage, int k, const u32x4 (&row)[RCH]) {
     char* buf = ring + stage * TILE_BYTES;
     for (int kk = k; kk < TT; ++kk) {
-      const int sw = FP8 ? sd_swz4(kk) : sd_swz(kk);
+      const int sw = FP8 ? fp8_chunk_swz(kk) : row_chunk_swz(kk);
 #pragma unroll
       for (int r = 0; r < RCH; ++r) {
         const int c = lane + 64 * r;

@@ -33,6 +33,7 @@
 //         16-key half), P^T in the same key order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_layout.hpp"
 
 namespace pa {
 namespace stk {
@@ -43,14 +44,8 @@ constexpr int NST = 4;                 // ring stages (two steps of two tiles)
 constexpr int DK = 576, DV = 512;      // latent row; V = its first DV columns
 }  // namespace stk
 
-// XOR swizzle of a row's 16-byte chunk index within groups of 8 chunks: key & 6.  Rows of
-// 1152 bytes put odd keys 128 bytes (mod 256) past even ones, and the LDS (64 banks of 4
-// bytes) serves a 64-bit read 32 lanes at a time: the transposing V^T read's 8 keys per 32
-// lanes then take four different 32-byte chunk pairs per key parity, covering the 64
-// banks once, and the 16-byte K reads of 16 consecutive keys stay conflict-free (both
-// measured with the LDS bank-conflict counter).  It depends on the row mod 16 only, so
-// both 16-key halves of a tile share it.
-__device__ __forceinline__ int tok_swz(int key) { return key & 6; }
+// The ring rows (1152 bytes) use lds_layout.hpp's row_chunk_swz: it depends on the row mod
+// 16 only, so both 16-key halves of a tile share it.
 
 __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitArgs a) {
   using namespace stk;
@@ -121,7 +116,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
       const int u = tw * SHARE + i;
       const int slot = u * 64 + ln;
       const int key = slot / CH;
-      const int c = (slot - key * CH) ^ tok_swz(key);
+      const int c = (slot - key * CH) ^ row_chunk_swz(key);
       dma16_nt_s((uint32_t)((min(key, kmax) - r0) * ssb + c * 16), base, lds_addr(buf + u * 1024));
     }
   };
@@ -150,14 +145,14 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   // lane byte offsets inside a tile: K operand chunk 4ks+g of key n (per ks parity; the
   // rest of ks is an immediate) and the transposed V source (per 16-dim block, mod 4);
   // the second 16-key half is 16 rows further
-  const int sw = tok_swz(n);
+  const int sw = row_chunk_swz(n);
   int koff[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) koff[par] = (n * CH + ((4 * par + g) ^ sw)) * 16;
   int voff[4];
   {
     const int vkey = 4 * g + (n >> 2);
-    const int vsw = tok_swz(vkey);
+    const int vsw = row_chunk_swz(vkey);
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
       const int ch = 2 * d4 + ((n & 3) >> 1);      // chunk of dims 16*d4 + 4*(n&3)
