@@ -15,10 +15,11 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
-# the same library with the decode kernel's per-wave phase stamps compiled in (diagnostics
-# only: bench.py --phase-stamps loads it; the entry points' library never carries them)
+# the same library with the decode and fp8-verify kernels' per-wave phase stamps compiled in
+# (diagnostics only: bench.py --phase-stamps loads it; the entry points' library never
+# carries them)
 STAMPS_LIB = os.path.join(HERE, "libpagedattn_stamps.so")
-STAMPED_SOURCE = "splitkv_dma.hip"
+STAMPED_SOURCES = ("splitkv_dma.hip", "splitkv_wide.hip")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip",
            "prefill.hip"]
@@ -63,12 +64,12 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library (and its phase-stamped twin);
     returns the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = [(src, (), "") for src in SOURCES] + [(STAMPED_SOURCE, ("-DPA_PHASE_STAMPS",), ".stamps")]
+    jobs = [(src, (), "") for src in SOURCES] + [(src, ("-DPA_PHASE_STAMPS",), ".stamps") for src in STAMPED_SOURCES]
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
     _link(objs[:len(SOURCES)], LIB)
-    stamped = [objs[-1] if src == STAMPED_SOURCE else o for src, o in zip(SOURCES, objs)]
-    _link(stamped, STAMPS_LIB)
+    stamped_obj = dict(zip(STAMPED_SOURCES, objs[len(SOURCES):]))
+    _link([stamped_obj.get(src, o) for src, o in zip(SOURCES, objs)], STAMPS_LIB)
     if verbose:
         print(f"built {LIB} and {os.path.basename(STAMPS_LIB)}")
     return LIB

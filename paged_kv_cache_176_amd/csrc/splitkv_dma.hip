@@ -26,49 +26,12 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_layout.hpp"
+#include "phase_stamps.hpp"
 
 namespace pa {
 
-// ---- phase stamps: an instrumented build only (compiled with -DPA_PHASE_STAMPS into
-// libpagedattn_stamps.so; the library the entry points ship in has none of this).  Every
-// wave keeps up to 64 s_memrealtime readings (100 MHz) in one register, lane k holding
-// stamp k, and stores them at its end to g_phase_stamps[(workgroup * 4 + wave) * 64 + k]
-// (workgroup = (z * gridDim.y + y) * gridDim.x + x; waves past kStampWaves are not kept):
-//   0 entry, 1 ring prologue issued, 2 Q and the first tiles landed, 3 + 2i / 4 + 2i the
-//   wave's i-th tile after its wait / after its compute (i < 27; later tiles overwrite the
-//   27th), 58 tiles consumed, 59 XCC id, 60 loop end, 61 first epilogue barrier passed,
-//   62 end, 63 HW_ID ----
 #ifdef PA_PHASE_STAMPS
-constexpr int kStampWaves = 1 << 14;
-__device__ uint32_t g_phase_stamps[kStampWaves * 64];
-#define PA_STAMP_DECL uint32_t st_ = 0; int it_ = 0;
-#define PA_STAMP(k)                                                            \
-  {                                                                            \
-    const uint32_t t_ = (uint32_t)__builtin_amdgcn_s_memrealtime();            \
-    st_ = lane == (k) ? t_ : st_;                                              \
-  }
-#define PA_STAMP_TILE_WAITED PA_STAMP(3 + 2 * it_)
-#define PA_STAMP_TILE_DONE                                                     \
-  {                                                                            \
-    PA_STAMP(4 + 2 * it_);                                                     \
-    it_ = it_ < 27 ? it_ + 1 : it_;                                            \
-  }
-#define PA_STAMP_FLUSH                                                         \
-  {                                                                            \
-    PA_STAMP(62);                                                              \
-    const uint32_t hw_ = __builtin_amdgcn_s_getreg((31 << 11) | 4);           \
-    const uint32_t xcc_ = __builtin_amdgcn_s_getreg((31 << 11) | 20);         \
-    st_ = lane == 63 ? hw_ : lane == 59 ? xcc_ : lane == 58 ? (uint32_t)it_ : st_; \
-    const int64_t wg_ = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x; \
-    const int64_t w_ = wg_ * sd::NW + wave;                                    \
-    if (w_ < kStampWaves) g_phase_stamps[w_ * 64 + lane] = st_;                \
-  }
-#else
-#define PA_STAMP_DECL
-#define PA_STAMP(k)
-#define PA_STAMP_TILE_WAITED
-#define PA_STAMP_TILE_DONE
-#define PA_STAMP_FLUSH
+__device__ uint32_t g_phase_stamps[kStampWaves * 64];   // this kernel's stamps (phase_stamps.hpp)
 #endif
 
 namespace sd {
@@ -170,7 +133,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       for (int c = lane; c < CH; c += 64) *reinterpret_cast<u32x4*>(row + c * 16) = new_row_chunk(c);
     }
     write_empty_partials<(DK > 256)>(a, q0, 0, min(min(L, a.max_q), ROWS / G), G, kvh, part, DV, NW * 64);
-    PA_STAMP_FLUSH
+    PA_STAMP_FLUSH(g_phase_stamps, sd::NW)
     return;
   }
 
@@ -524,7 +487,7 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
                      (M == kNegInf || Ls == 0.f) ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2);
     }
   }
-  PA_STAMP_FLUSH
+  PA_STAMP_FLUSH(g_phase_stamps, sd::NW)
 }
 
 // Eligible shapes: DiffKV rows, bf16 or fp8 (up to 32 rows per KV head), and bf16 MLA

@@ -25,8 +25,12 @@
 // conflict-free on the 20-chunk row pitch.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "phase_stamps.hpp"
 
 namespace pa {
+#ifdef PA_PHASE_STAMPS
+__device__ uint32_t g_phase_stamps_wide[kStampWaves * 64];   // this kernel's stamps (phase_stamps.hpp)
+#endif
 namespace sw {
 constexpr int TT = 32;       // keys per tile
 constexpr int DK = 192, DV = 128;
@@ -67,6 +71,8 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int n = lane & 31, g = lane >> 5;        // MFMA column (query row) and k-group
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
+  PA_STAMP_DECL
+  PA_STAMP(0)
   // the per-sequence scalars in one round trip (a NULL qsl reads zeros)
   const int32_t* qslp = a.qsl ? a.qsl + b : reinterpret_cast<const int32_t*>(kZeroScalars);
   const int S = load_uniform(a.seq_lens + b);
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   const int32_t* btrow = a.bt + (int64_t)b * a.bt_stride;
   if (nt == 0) {                                 // an empty key range: empty partials at once
     write_empty_partials<true>(a, q0, 0, min(min(L, a.max_q), ROWS / G), G, kvh, part, DV, NW * 64);
+    PA_STAMP_FLUSH(g_phase_stamps_wide, NW)
     return;
   }
 
@@ -152,6 +159,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   for (int k = 0; k < NST; ++k)
     if (wave + k * NW < nt) issue(wave + k * NW, k);
 
+  PA_STAMP(1)
   // ---- Q row n (B operand): k-step ks holds dims 32(ks/2) + 16g + 8(ks%2) .. +8, the
   // order in which one 16-byte fp8 chunk of K feeds two k-steps ----
   const int qi = n / G, hh = n - qi * G;
@@ -198,6 +206,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   // count DMA instructions only, and the compiler, which counts only the loads it
   // issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
+  PA_STAMP(2)
 
   auto compute = [&](int ti, int stage) {
     const char* buf = ring + stage * TILE_BYTES;
@@ -276,7 +285,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
       if (NST > 2 && later >= 2) wait_vm<(NST > 2 ? 2 : 0) * NINS>();
       else if (later >= 1) wait_vm<NINS>();
       else wait_vm<0>();
+      PA_STAMP_TILE_WAITED
       compute(ti, stage);
+      PA_STAMP_TILE_DONE
       stage = (stage + 1) % NST;
     }
   }
@@ -284,12 +295,14 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
   // ---- merge the NW waves: each writes its scaled accumulator to its own LDS slab
   // (independent stores, no read-modify-write chain), then all threads sum the slabs
   // in wave order and write the partials of the live rows ----
+  PA_STAMP(60)
   {
     float x = l, y = l;                          // row n's two halves of the keys
     swap_rows32(x, y);
     l = x + y;
   }
   __syncthreads();                               // rings are dead from here on
+  PA_STAMP(61)
   float* mw = reinterpret_cast<float*>(smem);    // [NW][ROWS]
   float* lw = mw + NW * ROWS;                    // [NW][ROWS]
   float* slab = lw + NW * ROWS;                  // [NW][ROWS][MERGE_PITCH]
@@ -334,6 +347,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
                      (Mx == kNegInf || Lx == 0.f) ? kNegInf : (Mx + __builtin_log2f(Lx)) * kLn2);
     }
   }
+  PA_STAMP_FLUSH(g_phase_stamps_wide, NW)
 }
 
 // fp8 DiffKV rows with 17..32 query rows per KV head, power-of-two block size >= 16.
@@ -351,3 +365,12 @@ void launch_splitkv_wide(const SplitArgs& a, hipStream_t s) {
 }
 
 }  // namespace pa
+
+#ifdef PA_PHASE_STAMPS
+// The fp8 verify kernel's stamps (layout in phase_stamps.hpp): copies the first `words`
+// (at most kStampWaves * 64) to host memory `dst`; returns the hipError_t of the copy.
+extern "C" int attn_phase_stamps_read_wide(void* dst, size_t words) {
+  if (!dst || words > (size_t)pa::kStampWaves * 64) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(pa::g_phase_stamps_wide), words * 4, 0, hipMemcpyDeviceToHost);
+}
+#endif

@@ -43,17 +43,17 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_phase_stamped_twin_exports_the_same_calls_plus_the_stamp_reader():
-    """The diagnostics library (decode kernel with phase stamps) is a drop-in twin: every
-    declared call, plus attn_phase_stamps_read, which the product library does not carry."""
+    """The diagnostics library (decode and fp8-verify kernels with phase stamps) is a drop-in twin:
+    every declared call, plus the two stamp readers, which the product library does not carry."""
     from paged_kv_cache_176_amd import build as pkb
     assert os.path.exists(pkb.STAMPS_LIB), "libpagedattn_stamps.so is not built"
     nm = lambda p: set(re.findall(r"\sT\s(\w+)$", subprocess.run(["nm", "-D", "--defined-only", p],
                                                                   capture_output=True, text=True).stdout, flags=re.M))
     twin, product = nm(pkb.STAMPS_LIB), nm(pk.library_path())
     assert set(declared_functions()) <= twin
-    assert "attn_phase_stamps_read" in twin and "attn_phase_stamps_read" not in product
-    assert {n for n in product if n.startswith("attn_")} == {n for n in twin if n.startswith("attn_")} - {
-        "attn_phase_stamps_read"}
+    readers = {"attn_phase_stamps_read", "attn_phase_stamps_read_wide"}
+    assert readers <= twin and not readers & product
+    assert {n for n in product if n.startswith("attn_")} == {n for n in twin if n.startswith("attn_")} - readers
 
 
 def test_struct_layout_matches_header(lib):
