@@ -594,16 +594,16 @@ def sample_clocks(fn, seconds=1.5):
     import subprocess
     import threading
     import torch
-    box = {}
+    sample = {}
 
     def probe():
         time.sleep(seconds / 2)
         try:
             r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0", "--json"], capture_output=True, text=True,
                                timeout=20)
-            box["json"] = r.stdout
+            sample["json"] = r.stdout
         except Exception as e:                       # noqa: BLE001 - the clocks are informative only
-            box["err"] = str(e)
+            sample["err"] = str(e)
 
     th = threading.Thread(target=probe)
     th.start()
@@ -616,7 +616,7 @@ def sample_clocks(fn, seconds=1.5):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     th.join()
-    return parse_clocks(box.get("json"))
+    return parse_clocks(sample.get("json"))
 
 
 def parse_clocks(text):
