@@ -451,9 +451,9 @@ def run_mla(batch, steps, warmup, cpu=True):
                        cpu_sample=f"1 of the {batch} sequences (fp64 attention over its 100000 keys), x{batch}")
 
 
-def run_mla_verify(batch, steps, warmup, qlen=4, cpu=True):
-    """MLA verify: qlen query tokens per sequence (drafts + 1) over the 12-head latent
-    cache, S = 100000, rotating cache copies; one attn_verify call (partials, then the merge)."""
+def mla_verify_calls(batch, qlen=4):
+    """The MLA verify workload resident on the GPU (cache copies rotated past the MALL) and one
+    prepared attn_verify call per copy; returns (workload, calls, P)."""
     import torch
     import paged_kv_cache_176_amd as pk
     import workloads
@@ -475,6 +475,13 @@ def run_mla_verify(batch, steps, warmup, qlen=4, cpu=True):
 
     calls = [pk.verify(q, qsl, sl, bt, d, w.softmax_scale, qlen, P, out=out, workspace=ws, with_lse=False,
                        prepare=True) for d in descs]
+    return w, calls, P
+
+
+def run_mla_verify(batch, steps, warmup, qlen=4, cpu=True):
+    """MLA verify: qlen query tokens per sequence (drafts + 1) over the 12-head latent
+    cache, S = 100000, rotating cache copies; one attn_verify call (partials, then the merge)."""
+    w, calls, P = mla_verify_calls(batch, qlen)
 
     def one(i, ev):
         if ev is not None:
@@ -796,50 +803,62 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-STAMP_CASES = {   # name -> (workload, KV heads, the launch's split count)
-    "decode_b1": (lambda w: w.long_decode(1, 131072, 16), 4, lambda: auto_partitions(1, 4, 131072, wgs_per_cu=2)),
-    "decode_b8": (lambda w: w.long_decode(8, 8192, 16), 4, lambda: auto_partitions(8, 4, 8192, wgs_per_cu=2)),
-    "mla_b1": (lambda w: w.mla_decode(1, 100000), 1, lambda: auto_partitions(1, 1, 100000)),
-    "mla_b16": (lambda w: w.mla_decode(16, 100000), 1, lambda: auto_partitions(16, 1, 100000)),
-    "fp8_verify": (None, 4, lambda: auto_partitions(4, 4, 46080)),   # the fp8 verify kernel's own stamps
+STAMP_CASES = {   # name -> (kernel's stamp reader, waves per workgroup, setup returning (grid size, launch fn))
+    "decode_b1": ("attn_phase_stamps_read", 4, lambda: _stamp_decode(lambda w: w.long_decode(1, 131072, 16), 4, 2)),
+    "decode_b8": ("attn_phase_stamps_read", 4, lambda: _stamp_decode(lambda w: w.long_decode(8, 8192, 16), 4, 2)),
+    "mla_b1": ("attn_phase_stamps_read", 4, lambda: _stamp_decode(lambda w: w.mla_decode(1, 100000), 1, 1)),
+    "mla_b16": ("attn_phase_stamps_read", 4, lambda: _stamp_decode(lambda w: w.mla_decode(16, 100000), 1, 1)),
+    "fp8_verify": ("attn_phase_stamps_read_wide", 4, lambda: _stamp_fp8_verify()),
+    "mla_verify_b1": ("attn_phase_stamps_read_tokens", 8, lambda: _stamp_mla_verify(1)),
+    "mla_verify_b16": ("attn_phase_stamps_read_tokens", 8, lambda: _stamp_mla_verify(16)),
 }
 
 
+def _stamp_decode(make, kv_heads, wgs_per_cu):
+    import workloads
+    w = make(workloads)
+    B, S = int(w.seq_lens.numel()), int(w.seq_lens.max())
+    P = auto_partitions(B, kv_heads, S, wgs_per_cu=wgs_per_cu)
+    c = DecodeCase(w, P)
+    return P, P * kv_heads * B, c.partial
+
+
+def _stamp_fp8_verify():
+    P = auto_partitions(4, 4, 46080)
+    w, calls = fp8_verify_calls("tensor", P)
+    return P, P * 4 * int(w.seq_lens.numel()), lambda i: calls[i % len(calls)]()
+
+
+def _stamp_mla_verify(batch):
+    w, calls, P = mla_verify_calls(batch)
+    return P, P * 1 * batch, lambda i: calls[i % len(calls)]()   # one token group of 4 per sequence
+
+
 def phase_stamps(name, launches=40):
-    """Per-wave phase timeline of the decode (or fp8 verify) partial kernel, from the library built
-    with its phase stamps (the last of `launches` back-to-back launches of the partial kernel):
-    percentiles over all waves of each phase's time from the first wave's entry, of the
-    per-tile wait and compute, and the end time per XCC."""
+    """Per-wave phase timeline of a split-KV partial kernel (decode, fp8 verify or MLA verify),
+    from the library built with the kernels' phase stamps (the last of `launches` back-to-back
+    launches): percentiles over the waves of each phase's time from the first wave's entry, of the
+    per-tile (per-step for MLA verify) wait and compute, and the end time per XCC."""
     import ctypes
     import numpy as np
     import torch
     import paged_kv_cache_176_amd as pk
-    import workloads
     lib = pk.load_library()
-    make, hkv, parts = STAMP_CASES[name]
-    P = parts()
-    if make is None:                                   # fp8 verify: its kernel, its reader
-        w, calls = fp8_verify_calls("tensor", P)
-        for i in range(launches):
-            calls[i % len(calls)]()
-        reader = lib.attn_phase_stamps_read_wide
-    else:
-        w = make(workloads)
-        c = DecodeCase(w, P)
-        for i in range(launches):
-            c.partial(i)
-        reader = lib.attn_phase_stamps_read
+    reader_name, wpw, setup = STAMP_CASES[name]
+    P, wgs, launch = setup()
+    for i in range(launches):
+        launch(i)
+    reader = getattr(lib, reader_name)
+    waves = wgs * wpw
+    buf = np.zeros(waves * 64, dtype=np.uint32)
     torch.cuda.synchronize()
     reader.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    waves = P * hkv * int(w.seq_lens.numel()) * 4
-    buf = np.zeros(waves * 64, dtype=np.uint32)
     rc = reader(buf.ctypes.data, buf.size)
     if rc != 0:
         raise RuntimeError(f"reading the phase stamps failed ({rc})")
     st = buf.reshape(waves, 64).astype(np.int64)
-    if make is None:       # the workgroups of the padded rows (no key) exit at once: left out
-        st = st[st[:, 58] > 0]
-        waves = len(st)
+    st = st[st[:, 58] > 0]             # workgroups with no key (the padded verify rows) exit at once
+    waves = len(st)
     rel = (st - st[:, 0].min()) * 0.01                 # s_memrealtime ticks at 100 MHz -> us
     q = lambda a: {k: round(float(np.percentile(a, v)), 2) for k, v in (("min", 0), ("p10", 10), ("p50", 50),
                                                                          ("p90", 90), ("max", 100))}

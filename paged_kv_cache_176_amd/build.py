@@ -15,11 +15,11 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
-# the same library with the decode and fp8-verify kernels' per-wave phase stamps compiled in
+# the same library with the decode, fp8-verify and MLA-verify kernels' per-wave phase stamps compiled in
 # (diagnostics only: bench.py --phase-stamps loads it; the entry points' library never
 # carries them)
 STAMPS_LIB = os.path.join(HERE, "libpagedattn_stamps.so")
-STAMPED_SOURCES = ("splitkv_dma.hip", "splitkv_wide.hip")
+STAMPED_SOURCES = ("splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip",
            "prefill.hip"]

@@ -34,8 +34,12 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_layout.hpp"
+#include "phase_stamps.hpp"
 
 namespace pa {
+#ifdef PA_PHASE_STAMPS
+__device__ uint32_t g_phase_stamps_tokens[kStampWaves * 64];   // this kernel's stamps (phase_stamps.hpp)
+#endif
 namespace stk {
 constexpr int NTOK = 4;                // query tokens per workgroup
 constexpr int NW = 2 * NTOK;           // waves: two per token
@@ -67,6 +71,8 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int tw = wave & (NTOK - 1), h = wave / NTOK;   // token slot, key half
+  PA_STAMP_DECL
+  PA_STAMP(0)
   const int P = a.num_partitions;
   const int G = a.num_q_heads / a.c.num_kv_heads;
   // the per-sequence scalars in one round trip (a NULL qsl reads zeros)
@@ -76,13 +82,17 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   const int q0 = a.qsl ? qs0 : b;
   const int L = a.qsl ? qs1 - qs0 : 1;
   const int Lq = min(L, a.max_q);
-  if (tg * NTOK >= Lq) return;                     // no token of this sequence here (uniform)
+  if (tg * NTOK >= Lq) {                           // no token of this sequence here (uniform)
+    PA_STAMP_FLUSH(g_phase_stamps_tokens, NW)
+    return;
+  }
   const int chunk = ceil_div(ceil_div(S, active_splits(a.pol, S, P)), 16) * 16;
   const int start = min(part * chunk, S);
   const int end = min(start + chunk, S);
   const int nt = ceil_div(end - start, TT);
   if (nt == 0) {                                 // an empty key range: empty partials at once
     write_empty_partials<true>(a, q0, tg * NTOK, min(NTOK, Lq - tg * NTOK), G, kvh, part, DV, NW * 64);
+    PA_STAMP_FLUSH(g_phase_stamps_tokens, NW)
     return;
   }
   const int nsteps = ceil_div(nt, 2);
@@ -122,6 +132,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   };
   // prologue: steps 0 and 1 (tiles 0..3), each wave its share of its half's tiles
   for (int k = h; k < min(NST, nt); k += 2) issue(k);
+  PA_STAMP(1)
 
   // ---- the token's Q rows (B operand; heads >= G are zero rows) ----
   bf16x8 qreg[KS];
@@ -168,6 +179,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   // Q and this wave's prologue shares are complete from here on (the compiler, which does
   // not count the DMA, sees this wait and adds none of its own for Q)
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+  PA_STAMP(2)
 
   // tile k; then, after the QK^T MFMAs, this wave's share of tile kn (kn < 0: none)
   auto compute = [&](int k, int kn) {
@@ -254,16 +266,20 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     const int k = 2 * j + h;                       // this wave's tile
     if (j >= 2) wait_vm<0>();                      // its share was issued at step j - 1
     __syncthreads();
+    PA_STAMP_TILE_WAITED
     const int kn = 2 * (j + 1) + h;
     const bool refill = j >= 1 && kn < nt;
     if (live && k < nt) compute(k, refill ? kn : -1);
     else if (refill) issue(kn);
+    PA_STAMP_TILE_DONE
   }
 
   // ---- the token's two halves merge through LDS: half 1 leaves (m, l, acc), half 0
   // combines them and writes the normalised partial and log-sum-exp ----
+  PA_STAMP(60)
   l = sum_over_groups(l);
   __syncthreads();                                 // the ring is free from here on
+  PA_STAMP(61)
   float* slab = reinterpret_cast<float*>(ring) + tw * 16 * SLAB_PITCH;
   float* ml = reinterpret_cast<float*>(ring) + NTOK * 16 * SLAB_PITCH + tw * 32;
   if (h == 1) {
@@ -292,6 +308,7 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     }
     if (g == 0) store_partial1<true>(a.part_lse + rh * P + part, empty ? kNegInf : (M + __builtin_log2f(Ls)) * kLn2);
   }
+  PA_STAMP_FLUSH(g_phase_stamps_tokens, NW)
 }
 
 // bf16 MLA rows, 2 or more query tokens, up to 16 query heads per KV head, power-of-two
@@ -310,3 +327,13 @@ void launch_splitkv_tokens(const SplitArgs& a, hipStream_t s) {
 }
 
 }  // namespace pa
+
+#ifdef PA_PHASE_STAMPS
+// The MLA verify token kernel's stamps (layout in phase_stamps.hpp; 8 waves per workgroup, a
+// "tile" is one step of the wave): copies the first `words` (at most kStampWaves * 64) to
+// host memory `dst`; returns the hipError_t of the copy.
+extern "C" int attn_phase_stamps_read_tokens(void* dst, size_t words) {
+  if (!dst || words > (size_t)pa::kStampWaves * 64) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(pa::g_phase_stamps_tokens), words * 4, 0, hipMemcpyDeviceToHost);
+}
+#endif

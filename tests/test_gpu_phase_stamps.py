@@ -1,4 +1,4 @@
-"""The phase-stamped diagnostics build of the decode kernel runs and gives a consistent
+"""The phase-stamped diagnostics build of the split-KV partial kernels runs and gives a consistent
 per-wave timeline (bench.py --phase-stamps, in a process of its own since it loads the
 stamped twin of the library)."""
 import json
@@ -14,8 +14,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # tiles per wave: B8 512 keys per partition / 16-key tiles / 4 waves; MLA B1 448 keys per
 # partition (7 per wave), the last partition 100000 - 223 x 448 = 96 keys (2, 2, 1, 1)
-# fp8 verify: 46080 keys / 16 partitions = 2880 keys = 90 tiles of 32 keys over 4 waves (23, 23, 22, 22)
-@pytest.mark.parametrize("name,tiles", [("decode_b8", [8]), ("mla_b1", [1, 2, 7]), ("fp8_verify", [22, 23])])
+# fp8 verify: 46080 keys / 16 partitions = 2880 keys = 90 tiles of 32 keys over 4 waves (23, 23, 22, 22);
+# MLA verify B1 (steps of two 32-key tiles): 448 keys = 7 steps, the last partition's 96 keys 2 steps
+@pytest.mark.parametrize("name,tiles", [("decode_b8", [8]), ("mla_b1", [1, 2, 7]), ("fp8_verify", [22, 23]),
+                                        ("mla_verify_b1", [2, 7])])
 def test_phase_timeline(name, tiles):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--phase-stamps", name],
                        capture_output=True, text=True, timeout=240, cwd=ROOT)

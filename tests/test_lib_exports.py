@@ -43,15 +43,15 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_phase_stamped_twin_exports_the_same_calls_plus_the_stamp_reader():
-    """The diagnostics library (decode and fp8-verify kernels with phase stamps) is a drop-in twin:
-    every declared call, plus the two stamp readers, which the product library does not carry."""
+    """The diagnostics library (decode, fp8-verify and MLA-verify kernels with phase stamps) is a
+    drop-in twin: every declared call, plus the stamp readers, which the product library does not carry."""
     from paged_kv_cache_176_amd import build as pkb
     assert os.path.exists(pkb.STAMPS_LIB), "libpagedattn_stamps.so is not built"
     nm = lambda p: set(re.findall(r"\sT\s(\w+)$", subprocess.run(["nm", "-D", "--defined-only", p],
                                                                   capture_output=True, text=True).stdout, flags=re.M))
     twin, product = nm(pkb.STAMPS_LIB), nm(pk.library_path())
     assert set(declared_functions()) <= twin
-    readers = {"attn_phase_stamps_read", "attn_phase_stamps_read_wide"}
+    readers = {"attn_phase_stamps_read", "attn_phase_stamps_read_wide", "attn_phase_stamps_read_tokens"}
     assert readers <= twin and not readers & product
     assert {n for n in product if n.startswith("attn_")} == {n for n in twin if n.startswith("attn_")} - readers
 
