@@ -24,8 +24,10 @@
 // each: a wave's share lies in one 16-key half, hence in one block).  A wave waits for its
 // own share, one workgroup barrier per step publishes the step's tiles and frees the
 // stages of the step before, which the same step refills with step j + 1: each wave
-// issues its share between its QK^T and PV MFMAs, so that the 8 waves' loads do not all
-// queue at the barrier and the issue overlaps MFMA work.
+// issues its share after the third k-step of its QK^T chains, so that the loads have
+// nearly the whole step to land (issued between QK^T and PV, they had only the PV's time
+// and the next step waited for them) while the 8 waves' loads still do not all queue at
+// the barrier.
 //   QK^T  S^T[16 keys x 16 rows] = K Q^T per 16-key half (two independent MFMA chains),
 //         v_mfma_f32_16x16x32_bf16, K from LDS (ds_read_b128, XOR-swizzled chunks).
 //   PV    O^T[16 dims x 16 rows] += V^T P^T over the 32 keys at once,
@@ -181,7 +183,10 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
   PA_STAMP(2)
 
-  // tile k; then, after the QK^T MFMAs, this wave's share of tile kn (kn < 0: none)
+  // tile k, and this wave's share of tile kn (kn < 0: none) issued after k-step
+  // kIssueStep of the QK^T chains (MLA verify B1 call -3%, B16 kernel -1.4% against the
+  // issue after the last k-step; issuing right after the barrier: -3% and -0.6%)
+  constexpr int kIssueStep = 2;
   auto compute = [&](int k, int kn) {
     const char* buf = ring + (k & (NST - 1)) * TILE_BYTES;
     const int j0 = start + k * TT;
@@ -206,8 +211,8 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0[ks % (KPF + 1)], qreg[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1[ks % (KPF + 1)], qreg[ks], s1, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (ks == kIssueStep && kn >= 0) issue(kn);  // the refill: behind three k-steps
     }
-    if (kn >= 0) issue(kn);
     // lane (n, g): keys j0 + 4g + i (s0) and j0 + 16 + 4g + i (s1) of row n.  A tile the
     // token sees whole needs no mask, and the scale folds into one fma
     const bool nomask = j0 + TT - 1 <= hi;
