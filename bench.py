@@ -687,6 +687,8 @@ def main():
     ap.add_argument("--phase-stamps", choices=sorted(STAMP_CASES), default=None,
                     help="load the library built with the partial kernels' phase stamps and print the per-wave "
                          "timeline of this workload (diagnostics; no timing line)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="print the matrix-core issue probe's table (libmfma_probe.so) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, one device-to-device copy of this many MiB (a kernel of known "
                          "size that calibrates hardware byte counters)")
@@ -700,6 +702,10 @@ def main():
     import torch
     import paged_kv_cache_176_amd as pk
     import workloads
+    if args.mfma_probe:
+        assert torch.cuda.is_available(), "bench.py needs the GPU"
+        print(json.dumps(mfma_probe()), flush=True)
+        return
     if args.phase_stamps:
         from paged_kv_cache_176_amd import build as pkb
         pk.ops.use_library(pkb.STAMPS_LIB)
@@ -832,6 +838,29 @@ def _stamp_fp8_verify():
 def _stamp_mla_verify(batch):
     w, calls, P = mla_verify_calls(batch)
     return P, P * 1 * batch, lambda i: calls[i % len(calls)]()   # one token group of 4 per sequence
+
+
+def mfma_probe():
+    """The matrix-core issue probe (libmfma_probe.so, built beside the library): for each
+    configuration, cycles per v_mfma_f32_32x32x16_bf16 per SIMD and, where a wave runs only
+    VALU beside an MFMA wave, that wave's cycles per instruction."""
+    import ctypes
+    from paged_kv_cache_176_amd import build as pkb
+    if not os.path.exists(pkb.PROBE_LIB):
+        raise RuntimeError(f"{pkb.PROBE_LIB} is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(pkb.PROBE_LIB)
+    lib.mfma_probe_label.restype = ctypes.c_char_p
+    lib.mfma_probe_run.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    rows = []
+    for i in range(lib.mfma_probe_count()):
+        res = (ctypes.c_double * 3)()
+        rc = lib.mfma_probe_run(i, res)
+        if rc != 0:
+            raise RuntimeError(f"mfma probe configuration {i} failed ({rc})")
+        rows.append({"config": lib.mfma_probe_label(i).decode(), "cycles_per_mfma_per_simd": round(res[0], 1),
+                     "valu_wave_cycles_per_instruction": round(res[1], 2) if res[1] >= 0 else None})
+    return {"probe": "v_mfma_f32_32x32x16_bf16 issue, 256 workgroups x 2000 iterations, s_memtime cycles",
+            "rows": rows}
 
 
 def phase_stamps(name, launches=40):

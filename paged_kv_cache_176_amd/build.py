@@ -20,6 +20,9 @@ LIB = os.path.join(HERE, "libpagedattn.so")
 # carries them)
 STAMPS_LIB = os.path.join(HERE, "libpagedattn_stamps.so")
 STAMPED_SOURCES = ("splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip")
+# the matrix-core issue probe (a measurement tool, bench.py --mfma-probe), its own library
+PROBE_LIB = os.path.join(HERE, "libmfma_probe.so")
+PROBE_SOURCE = "mfma_probe.hip"
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "cache_write.hip", "splitkv.hip", "splitkv_dma.hip", "splitkv_wide.hip", "splitkv_tokens.hip",
            "prefill.hip"]
@@ -61,17 +64,20 @@ def _link(objs, out: str) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library (and its phase-stamped twin);
-    returns the library's path."""
+    """Compile every source and link the shared library (and its phase-stamped twin, and
+    the matrix-core probe); returns the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = [(src, (), "") for src in SOURCES] + [(src, ("-DPA_PHASE_STAMPS",), ".stamps") for src in STAMPED_SOURCES]
+    jobs = ([(src, (), "") for src in SOURCES] + [(src, ("-DPA_PHASE_STAMPS",), ".stamps") for src in STAMPED_SOURCES]
+            + [(PROBE_SOURCE, (), "")])
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    _link(objs[:len(SOURCES)], LIB)
-    stamped_obj = dict(zip(STAMPED_SOURCES, objs[len(SOURCES):]))
+    n, ns = len(SOURCES), len(STAMPED_SOURCES)
+    _link(objs[:n], LIB)
+    stamped_obj = dict(zip(STAMPED_SOURCES, objs[n:n + ns]))
     _link([stamped_obj.get(src, o) for src, o in zip(SOURCES, objs)], STAMPS_LIB)
+    _link(objs[n + ns:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} and {os.path.basename(STAMPS_LIB)}")
+        print(f"built {LIB}, {os.path.basename(STAMPS_LIB)} and {os.path.basename(PROBE_LIB)}")
     return LIB
 
 

@@ -56,6 +56,26 @@ def test_phase_stamped_twin_exports_the_same_calls_plus_the_stamp_reader():
     assert {n for n in product if n.startswith("attn_")} == {n for n in twin if n.startswith("attn_")} - readers
 
 
+def test_mfma_probe_library_is_separate_and_lists_its_configurations():
+    """The matrix-core issue probe (bench.py --mfma-probe) lives in its own library: it exports
+    only its three calls, none of the attention entry points, and names its configurations
+    without a GPU."""
+    from paged_kv_cache_176_amd import build as pkb
+    assert os.path.exists(pkb.PROBE_LIB), "libmfma_probe.so is not built"
+    out = subprocess.run(["nm", "-D", "--defined-only", pkb.PROBE_LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert {"mfma_probe_count", "mfma_probe_label", "mfma_probe_run"} <= exported
+    assert not {n for n in exported if n.startswith("attn_")}
+    probe = ctypes.CDLL(pkb.PROBE_LIB)
+    probe.mfma_probe_label.restype = ctypes.c_char_p
+    n = probe.mfma_probe_count()
+    labels = [probe.mfma_probe_label(i) for i in range(n)]
+    assert n >= 10 and all(labels) and len(set(labels)) == n
+    assert probe.mfma_probe_label(n) is None and probe.mfma_probe_label(-1) is None
+    res = (ctypes.c_double * 3)()
+    assert probe.mfma_probe_run(n, res) == -1          # a bad index is rejected before the GPU
+
+
 def test_struct_layout_matches_header(lib):
     # data(8) + 8 x int32(32) + 3 x int64(24) + 2 x enum(8) + 2 pointers(16)
     assert ctypes.sizeof(ops._CacheDescC) == 88
