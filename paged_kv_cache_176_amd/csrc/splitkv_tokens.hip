@@ -253,14 +253,25 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
     l += ps;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    // V^T operands read three MFMAs ahead behind a scheduling barrier per MFMA (the compiler's
+    // own order read one ahead, so every PV MFMA waited most of an LDS round trip: B16 kernel
+    // -2% in paired runs, same registers)
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto vread = [&](int db) -> bf16x8 {
       const char* vp = buf + voff[db & 3] + (db >> 2) * 128;     // +64 dims per 4 blocks
       const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
       const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + HALF));
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb, acc[db], 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    constexpr int VPF = 3;
+    bf16x8 vq[VPF + 1];
+#pragma unroll
+    for (int q = 0; q < VPF; ++q) vq[q] = vread(q);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (db + VPF < DB) vq[(db + VPF) % (VPF + 1)] = vread(db + VPF);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vq[db % (VPF + 1)], pb, acc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
