@@ -97,10 +97,16 @@ def compare(out_gpu: torch.Tensor, ref: np.ndarray, fp8=False, lse_gpu=None, lse
     bound = 5e-2 if fp8 else 1e-2
     if strict:
         assert maxabs <= bound, f"{what}: max abs {maxabs}"
+        assert rmse <= 1e-3, f"{what}: rmse {rmse}"
     else:
-        excess = float((np.abs(err) - bf16_half_ulp(got)).max()) if err.size else 0.0
+        # small edge cases, whose outputs can be close to single V rows (|out| ~ 1): both bounds
+        # apply to the error beyond the bf16 output's own rounding, half a bf16 ulp of each
+        # output (rounding an exact |out| ~ 1 to bf16 alone gives an RMSE of ~2e-3)
+        beyond = np.maximum(np.abs(err) - bf16_half_ulp(got), 0.0)
+        excess = float(beyond.max()) if err.size else 0.0
         assert excess <= bound, f"{what}: max abs {maxabs} beyond the bf16 output rounding by {excess}"
-    assert rmse <= 1e-3, f"{what}: rmse {rmse}"
+        rmse_beyond = float(np.sqrt(np.mean(beyond ** 2))) if err.size else 0.0
+        assert rmse_beyond <= 1e-3, f"{what}: rmse {rmse}, {rmse_beyond} beyond the bf16 output rounding"
     if rms > 0:
         assert rmse / rms <= 1e-2, f"{what}: relative rmse {rmse / rms}"
         assert cos >= 0.9999, f"{what}: cosine {cos}"
