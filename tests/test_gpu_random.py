@@ -1,11 +1,11 @@
 """Randomised GPU parity sweep: seeded small cases over the shape space each entry point
 serves -- cache dtype and scale granularity, block size (powers of two and not), batch,
 ragged and empty sequences, GQA ratio, query tokens per sequence, split count, cache layout
-(NHD, HND, padded pitches), sink logits and a split policy -- each against the oracle on
-the same cache bytes.  The seeds are fixed; a failing case prints
-its parameters.  Kernel selection differs across these shapes (LDS-streamed, 32-row
-wide and register-prefetch split-KV kernels; fast and generic prefill), so the sweep
-crosses paths the hand-picked tests visit one at a time."""
+(NHD, HND, padded pitches), sink logits and a split policy, and the MLA decode and verify
+over random shapes -- each against the oracle on the same cache bytes.  The seeds are
+fixed; a failing case prints its parameters.  Kernel selection differs across these shapes
+(LDS-streamed, 32-row wide, MLA token and register-prefetch split-KV kernels; fast and
+generic prefill), so the sweep crosses paths the hand-picked tests visit one at a time."""
 import math
 import random
 
@@ -118,3 +118,41 @@ def test_random_prefill(gpu_lib, seed):
     out, lse = pk.prefill_causal(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len,
                                  sinks=None if sinks is None else sinks.to(DEV))
     compare(out, ref, fp8=kv == "fp8", lse_gpu=lse, lse_ref=ref_lse, what=what)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_mla(gpu_lib, seed):
+    """MLA decode and multi-token verify (one 576-wide latent KV head, V = its first 512 columns)
+    over random batches, lengths, query-head counts, draft lengths, block sizes, split counts,
+    layouts and sink logits; half the cases with queries 80x larger than the latent rows, so
+    the scores are peaked and a wrong causal limit or merge weight shows."""
+    rng = random.Random(5000 + seed)
+    bs = rng.choice([16, 32, 64])
+    G = rng.choice([8, 12, 12, 16])
+    B = rng.randint(1, 5)
+    verify = rng.random() < 0.6
+    qlens = [rng.randint(2, 8) if verify else 1 for _ in range(B)]
+    lens = [0 if rng.random() < 0.1 else rng.randint(L, 3000) for L in qlens]
+    qlens = [L if s else 1 for s, L in zip(lens, qlens)]
+    P = rng.choice([1, 2, 5, 16, 33, 64])
+    layout = rng.choice(["NHD", "NHD", "HND"])
+    pad = rng.choice([0, 0, 8, 64])
+    peaked = rng.random() < 0.5
+    sinks = None
+    if rng.random() < 0.3:
+        sinks = torch.tensor([rng.uniform(-4, 4) for _ in range(G)], dtype=torch.float32)
+    what = (f"seed {seed}: MLA {'verify' if verify else 'decode'} bs {bs} G {G} lens {lens} L {qlens} P {P} "
+            f"{layout} pad {pad}" + (" peaked" if peaked else "") + (" sinks" if sinks is not None else ""))
+    log(what)
+    g = workloads.mla_geom(0, bs, layout=layout, row_pad=pad)
+    w = workloads.paged_workload("mla_rand", g, lens, qlens, G, 1 / math.sqrt(576), seed=seed, std=0.1,
+                                 q_std=8.0 if peaked else None)
+    u = Uploaded(w)
+    u.write()
+    skd = None if sinks is None else sinks.to(DEV)
+    if verify:
+        out, lse, _ = pk.verify(u.q, u.qsl, u.seq_lens, u.bt, u.desc, w.softmax_scale, w.max_query_len, P, sinks=skd)
+    else:
+        out, lse, _ = pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, P, sinks=skd)
+    ref, ref_lse = oracle(w, u, sinks)
+    compare(out, ref, lse_gpu=lse, lse_ref=ref_lse, what=what)
