@@ -10,22 +10,25 @@
 // One thread moves one 8-element vector (16 B of bf16 in; 16 B bf16 or 8 B fp8
 // out).  The thread -> (token, head, vector) mapping is token-major so that a
 // wave covers whole rows and its loads and stores are contiguous.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace pa {
 
-template <bool FP8, bool VEC>
+// IDX: the flat item index type, 32-bit whenever the launch's item count fits (the divisions
+// by the per-token and per-head counts are then 32-bit, a fraction of the 64-bit sequence)
+template <bool FP8, bool VEC, typename IDX>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
   const int nk = VEC ? a.c.dk / 8 : a.c.dk;          // vectors (or elements) per head for K
   const int nv = a.value ? (VEC ? a.c.dv / 8 : a.c.dv) : 0;
   const int per_head = nk + nv;
   const int per_tok = per_head * a.c.num_kv_heads;
-  const int64_t total = (int64_t)per_tok * a.num_tokens;
-  for (int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; item < total;
-       item += (int64_t)gridDim.x * blockDim.x) {
-    const int t = (int)(item / per_tok);
-    const int r = (int)(item - (int64_t)t * per_tok);
+  const IDX total = (IDX)per_tok * (IDX)a.num_tokens;
+  for (IDX item = (IDX)blockIdx.x * blockDim.x + threadIdx.x; item < total; item += (IDX)gridDim.x * blockDim.x) {
+    const int t = (int)(item / (IDX)per_tok);
+    const int r = (int)(item - (IDX)t * (IDX)per_tok);
     const int h = r / per_head;
     const int c = r - h * per_head;
     const bool isk = c < nk;
@@ -46,8 +49,14 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a) {
     const int64_t slot = a.slots[t];
     if (slot < 0) continue;                          // padding token
     const int bs = a.c.block_size;
-    const int64_t blk = slot / bs;
-    const int64_t pos = slot - blk * bs;
+    int64_t blk, pos;
+    if ((bs & (bs - 1)) == 0) {                      // power-of-two block size: shifts
+      blk = slot >> __builtin_ctz(bs);
+      pos = slot & (bs - 1);
+    } else {
+      blk = slot / bs;
+      pos = slot - blk * bs;
+    }
     const int64_t row = blk * a.c.sb + pos * a.c.ss + (int64_t)h * a.c.sh;   // elements
     const int64_t dst_el = row + (isk ? 0 : a.c.v_off) + e0;
     if constexpr (!FP8) {
@@ -81,12 +90,21 @@ bool launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   dim3 grid((unsigned)blocks), block(256);
+  // 32-bit item indices while the last item plus one grid stride stays below 2^31
+  const bool narrow = total + (int64_t)blocks * 256 < ((int64_t)1 << 31);
+  auto go = [&](auto fp8_tag, auto vec_tag) {
+    constexpr bool F = decltype(fp8_tag)::value, V = decltype(vec_tag)::value;
+    if (narrow) hipLaunchKernelGGL((cache_write_kernel<F, V, uint32_t>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((cache_write_kernel<F, V, int64_t>), grid, block, 0, s, a);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
   if (fp8) {
-    if (vec) hipLaunchKernelGGL((cache_write_kernel<true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((cache_write_kernel<true, false>), grid, block, 0, s, a);
+    if (vec) go(T{}, T{});
+    else go(T{}, F{});
   } else {
-    if (vec) hipLaunchKernelGGL((cache_write_kernel<false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((cache_write_kernel<false, false>), grid, block, 0, s, a);
+    if (vec) go(F{}, T{});
+    else go(F{}, F{});
   }
   return true;
 }
