@@ -39,7 +39,7 @@ MALL_BYTES = 256 << 20
 # partition count they were taken at: any later change reports traffic as null until
 # re-measured.
 MEASURED_TRAFFIC = {
-    ("33ef23bbde1fc229", 128): 164006.6 * 1024 * 2 + 2178.7 * 1024,
+    ("304008f8c75d5565", 128): 164006.6 * 1024 * 2 + 2178.7 * 1024,
 }
 KERNEL_SOURCES = ("splitkv_dma.hip", "common.hpp", "kernels.hpp", "lds_layout.hpp", "phase_stamps.hpp")
 
@@ -894,18 +894,20 @@ def phase_stamps(name, launches=40):
     ntiles = st[:, 58]
     res = {"workload": name, "partitions": P, "waves": waves, "tiles_per_wave": sorted(set(ntiles.tolist())),
            "us_from_first_entry": {"entry": q(rel[:, 0]), "prologue_issued": q(rel[:, 1]),
-                                   "first_tiles_landed": q(rel[:, 2]), "loop_end": q(rel[:, 60]),
+                                   "q_landed": q(rel[:, 2]), "first_tile_ready": q(rel[:, 3]),
+                                   "loop_end": q(rel[:, 60]),
                                    "epilogue_barrier": q(rel[:, 61]), "end": q(rel[:, 62])}}
     tiles = []
     for k in range(min(int(ntiles.max()), 27)):       # over the waves that consume a k-th tile
         r = rel[ntiles > k]
-        wait = r[:, 3 + 2 * k] - (r[:, 2] if k == 0 else r[:, 4 + 2 * (k - 1)])
+        # tile 0 waits from the later of Q's landing and the prologue's issue
+        wait = r[:, 3 + 2 * k] - (np.maximum(r[:, 1], r[:, 2]) if k == 0 else r[:, 4 + 2 * (k - 1)])
         tiles.append({"tile": k, "waves": int(len(r)), "wait_us": q(wait),
                       "compute_us": q(r[:, 4 + 2 * k] - r[:, 3 + 2 * k])})
     res["tiles"] = tiles
     xcc = st[:, 59] & 0xF
     res["end_us_by_xcc"] = {int(x): q(rel[xcc == x, 62]) for x in np.unique(xcc)}
-    res["corr_first_tiles_vs_loop_end"] = round(float(np.corrcoef(rel[:, 2], rel[:, 60])[0, 1]), 3)
+    res["corr_first_tile_vs_loop_end"] = round(float(np.corrcoef(rel[:, 3], rel[:, 60])[0, 1]), 3)
     return res
 
 

@@ -4,7 +4,9 @@
 // lane k holding stamp k, and stores them at its end to the kernel's stamp array at
 // [(workgroup * waves per workgroup + wave) * 64 + k], workgroup = (z * gridDim.y + y) *
 // gridDim.x + x (waves past kStampWaves are not kept):
-//   0 entry, 1 ring prologue issued, 2 Q and the first tiles landed, 3 + 2i / 4 + 2i the
+//   0 entry, 1 ring prologue issued, 2 Q landed (the kernels that issue the ring first wait
+//   for Q and the prologue's tiles together, so there 2 follows 1; the kernels that load Q
+//   first issue the ring after Q's wait, so there 1 follows 2), 3 + 2i / 4 + 2i the
 //   wave's i-th tile after its wait / after its compute (i < 27; later tiles overwrite the
 //   27th), 58 tiles consumed, 59 XCC id, 60 loop end, 61 first epilogue barrier passed,
 //   62 end, 63 HW_ID.

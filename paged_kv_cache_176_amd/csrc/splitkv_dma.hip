@@ -178,12 +178,21 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
     }
   };
 
-  // every stage of the ring is filled before Q is loaded and before the first wait, so
-  // that the opening burst requests NST tiles per wave (a single tile per wave leaves
-  // HBM half idle until the first ones land)
+  // Every stage of the ring is issued before the first tile is waited for, so that the
+  // opening burst requests NST tiles per wave (a single tile per wave leaves HBM half idle
+  // until the first ones land).  Order against Q: the compiler does not count the DMA, so
+  // the wait it must see for Q (and the new row) is a vmcnt(0), which also covers every DMA
+  // issued before it.  DiffKV rows issue the ring first (that vmcnt(0) then waits for the
+  // whole prologue, but Q's round trip stays under the burst); MLA rows load Q first and
+  // issue the ring after its wait, so tile 0 is computed as soon as it lands instead of
+  // after the last prologue stage (MLA B1 step 29.2 -> 28.3 us; DiffKV B1/B8 ~1% slower
+  // that way, so they keep the first order).
+  constexpr bool kQFirst = DK > 256;
+  if constexpr (!kQFirst) {
 #pragma unroll
-  for (int k = 0; k < NST; ++k)
-    if (wave + k * NW < nt) issue(wave + k * NW, k);
+    for (int k = 0; k < NST; ++k)
+      if (wave + k * NW < nt) issue(wave + k * NW, k);
+  }
 
   u32x4 nrow[RCH];                               // the owner's new row, loaded with Q
 #pragma unroll
@@ -194,7 +203,9 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
       if (lane + 64 * r < CH) nrow[r] = new_row_chunk(lane + 64 * r);
   }
 
-  PA_STAMP(1)
+  if constexpr (!kQFirst) {
+    PA_STAMP(1)                                  // ring prologue issued
+  }
   // ---- Q rows (B operand), visibility limits ----
   bf16x8 qreg[NR][KS];
   int hi[NR];
@@ -263,11 +274,17 @@ __global__ __launch_bounds__(sd::NW * 64, MINW) void splitkv_dma_kernel(SplitArg
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Q and the first tiles are complete from here on: the explicit vmcnt waits below
-  // count DMA instructions only, and the compiler, which counts only the loads it
-  // issued, sees this wait and adds none of its own for Q
+  // Q is complete from here on (and, when the ring went first, the prologue's tiles): the
+  // explicit vmcnt waits below count DMA instructions only, and the compiler, which counts
+  // only the loads it issued, sees this wait and adds none of its own for Q
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-  PA_STAMP(2)
+  PA_STAMP(2)                                    // Q landed
+  if constexpr (kQFirst) {
+#pragma unroll
+    for (int k = 0; k < NST; ++k)
+      if (wave + k * NW < nt) issue(wave + k * NW, k);
+    PA_STAMP(1)                                  // ring prologue issued
+  }
   if (kPatchRow && own && wave == 0) {           // the new row into its cache slot
     uint8_t* row = new_row_base();
 #pragma unroll

@@ -132,9 +132,6 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
       dma16_nt_s((uint32_t)((min(key, kmax) - r0) * ssb + c * 16), base, lds_addr(buf + u * 1024));
     }
   };
-  // prologue: steps 0 and 1 (tiles 0..3), each wave its share of its half's tiles
-  for (int k = h; k < min(NST, nt); k += 2) issue(k);
-  PA_STAMP(1)
 
   // ---- the token's Q rows (B operand; heads >= G are zero rows) ----
   bf16x8 qreg[KS];
@@ -178,10 +175,15 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
-  // Q and this wave's prologue shares are complete from here on (the compiler, which does
-  // not count the DMA, sees this wait and adds none of its own for Q)
+  // Q is complete from here on (the compiler, which does not count the DMA, sees this wait
+  // and adds none of its own for Q).  Only then goes the prologue -- steps 0 and 1 (tiles
+  // 0..3), each wave its share of its half's tiles -- so that step 0 waits for its own
+  // share alone, not for step 1's as well (issued before Q, the prologue made this
+  // vmcnt(0) wait for both: the B1 call was 3% slower)
   __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-  PA_STAMP(2)
+  PA_STAMP(2)                                       // Q landed
+  for (int k = h; k < min(NST, nt); k += 2) issue(k);
+  PA_STAMP(1)                                       // ring prologue issued
 
   // tile k, and this wave's share of tile kn (kn < 0: none) issued after k-step
   // kIssueStep of the QK^T chains (MLA verify B1 call -3%, B16 kernel -1.4% against the
@@ -280,7 +282,8 @@ __global__ __launch_bounds__(stk::NW * 64, 1) void splitkv_tokens_kernel(SplitAr
   // consumes its tile of the step ----
   for (int j = 0; j < nsteps; ++j) {
     const int k = 2 * j + h;                       // this wave's tile
-    if (j >= 2) wait_vm<0>();                      // its share was issued at step j - 1
+    if (j == 0 && h + 2 < nt) wait_vm<SHARE>();   // step 0's share landed; step 1's may fly
+    else wait_vm<0>();                             // the share issued at step j - 1 (or the prologue's)
     __syncthreads();
     PA_STAMP_TILE_WAITED
     const int kn = 2 * (j + 1) + h;

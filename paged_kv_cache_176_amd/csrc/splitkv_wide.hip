@@ -152,14 +152,6 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     }
   };
 
-  // every stage of the ring is filled before Q is loaded and before the first wait, so
-  // that the opening burst requests NST tiles per wave (a single tile per wave leaves
-  // HBM half idle until the first ones land)
-#pragma unroll
-  for (int k = 0; k < NST; ++k)
-    if (wave + k * NW < nt) issue(wave + k * NW, k);
-
-  PA_STAMP(1)
   // ---- Q row n (B operand): k-step ks holds dims 32(ks/2) + 16g + 8(ks%2) .. +8, the
   // order in which one 16-byte fp8 chunk of K feeds two k-steps ----
   const int qi = n / G, hh = n - qi * G;
@@ -202,11 +194,18 @@ __global__ __launch_bounds__(NW * 64, MINW) void splitkv_wide_fp8_kernel(SplitAr
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  // Q and the first tiles are complete from here on: the explicit vmcnt waits below
-  // count DMA instructions only, and the compiler, which counts only the loads it
-  // issued, sees this wait and adds none of its own for Q
+  // Q and the scales are complete from here on: the compiler, which counts only the loads
+  // it issued, sees this wait and adds none of its own for them.  Only then is the ring
+  // issued -- every stage before the first tile is waited for, so the opening burst requests
+  // NST tiles per wave -- and the loop's explicit waits, which count DMA instructions only,
+  // let tile 0 be computed as soon as it lands.  (Issued before Q, the ring made this
+  // vmcnt(0) wait for all NST prologue tiles: the call was 4% slower.)
   __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
-  PA_STAMP(2)
+  PA_STAMP(2)                                    // Q landed
+#pragma unroll
+  for (int k = 0; k < NST; ++k)
+    if (wave + k * NW < nt) issue(wave + k * NW, k);
+  PA_STAMP(1)                                    // ring prologue issued
 
   auto compute = [&](int ti, int stage) {
     const char* buf = ring + stage * TILE_BYTES;
