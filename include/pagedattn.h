@@ -210,6 +210,8 @@ attn_status attn_decode_splitkv(const void* q, int64_t q_stride_tok, int64_t q_s
  *   read back).  A call whose attn_splitkv_workspace_bytes(num_seqs,
  *   num_q_heads, head_dim_v, num_partitions) exceeds the fixed size returns
  *   ATTN_E_INVALID before touching the GPU.
+ *   The workspace used is the one on the GPU that `stream` belongs to (the
+ *   current device's for the NULL stream).
  *   Every call on one GPU shares that GPU's workspace (it keeps the last call's
  *   partials): calls that overlap on one GPU -- on different streams, or from
  *   different threads -- race and must be ordered by the caller.  Its contents

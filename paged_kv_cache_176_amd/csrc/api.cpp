@@ -248,7 +248,8 @@ attn_status run_splitkv(const char* who, const void* q, int64_t q_st, int64_t q_
 // Split-KV workspace of attn_decode_splitkv_noalloc: a file-scope device array, so that the
 // call allocates nothing.  Each GPU holds its own copy (at its own address) from the first call
 // on it until the process ends.  In host code `scratch` is only a stand-in for the symbol: the
-// device address comes from hipGetSymbolAddress, taken once per device with that device current.
+// device address comes from hipGetSymbolAddress, taken once per device with that device current,
+// and a call uses the copy on the GPU its stream belongs to.
 constexpr size_t kScratchBytes = ATTN_NOALLOC_WORKSPACE_BYTES;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
@@ -256,21 +257,46 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// The current device's copy of `scratch`, or NULL with an error status in *st.
-void* scratch_for_current_device(const char* who, attn_status* st) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+// The copy of `scratch` on the GPU that runs `stream` (the current device for the NULL
+// stream), or NULL with an error status in *st.  The symbol's address is taken once per
+// device, with that device made current for the lookup and the caller's device restored.
+void* scratch_for_stream(hipStream_t stream, const char* who, attn_status* st) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess || cur < 0) {
     *st = fail(ATTN_E_HIP, "%s: no current HIP device (%s)", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess || d < 0) {
+      *st = fail(ATTN_E_HIP, "%s: cannot tell the stream's device (%s)", who, hipGetErrorString(e));
+      return nullptr;
+    }
+    dev = d;
+  }
+  if (dev >= kMaxDevices) {
+    *st = fail(ATTN_E_HIP, "%s: device %d is past the %d the library tracks", who, dev, kMaxDevices);
     return nullptr;
   }
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) {
+      *st = fail(ATTN_E_HIP, "%s: hipSetDevice(%d) failed: %s", who, dev, hipGetErrorString(e));
+      return nullptr;
+    }
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
     if (e != hipSuccess || !p) {
       *st = fail(ATTN_E_HIP, "%s: hipGetSymbolAddress of the workspace failed on device %d: %s", who, dev,
                  hipGetErrorString(e));
+      return nullptr;
+    }
+    if (back != hipSuccess) {
+      *st = fail(ATTN_E_HIP, "%s: restoring device %d failed: %s", who, cur, hipGetErrorString(back));
       return nullptr;
     }
     g_scratch_ptr[dev] = p;
@@ -347,7 +373,7 @@ attn_status attn_decode_splitkv_noalloc(const void* q, int64_t q_stride_tok, int
   void* ws = nullptr;
   if (num_seqs > 0) {
     attn_status st = ATTN_OK;
-    ws = scratch_for_current_device(who, &st);
+    ws = scratch_for_stream(static_cast<hipStream_t>(stream), who, &st);
     if (!ws) return st;
   }
   return run_splitkv(who, q, q_stride_tok, q_stride_head, nullptr, num_seqs, num_seqs, 1, num_q_heads, cache,

@@ -73,3 +73,45 @@ def test_noalloc_rejects_oversized_calls(gpu_lib):
     out = torch.empty(1, 32, 128, dtype=torch.bfloat16, device=u.q.device)
     with pytest.raises(pk.AttnError, match="over the fixed workspace"):
         pk.decode_splitkv_noalloc(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, 1100, out=out)
+
+
+def test_noalloc_on_a_side_stream_and_under_graph_capture(gpu_lib):
+    """The call on a stream other than the default one (the workspace is the copy on that
+    stream's GPU), and captured into a graph: every replay, with eager calls of another size
+    in between that overwrite the shared workspace, gives the eager result bit for bit."""
+    w = workloads.paged_workload("noalloc_graph", workloads.diffkv_geom(0, 16), [3000, 500], [1, 1], 32,
+                                 1 / math.sqrt(192), seed=95)
+    u = Uploaded(w)
+    u.write()
+    other = workloads.paged_workload("noalloc_other", workloads.diffkv_geom(0, 16), [1200, 40, 7], [1, 1, 1], 32,
+                                     1 / math.sqrt(192), seed=96)
+    uo = Uploaded(other)
+    uo.write()
+    P = 16
+    ref_out, ref_lse, _ = pk.decode_splitkv(u.q, u.desc, u.bt, u.seq_lens, w.softmax_scale, P)
+    torch.cuda.synchronize()
+    out = torch.full_like(ref_out, float("nan"))
+    lse = torch.full_like(ref_lse, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        c_noalloc(u, P, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), "side-stream call differs"
+
+    gout = torch.full_like(ref_out, float("nan"))
+    glse = torch.full_like(ref_lse, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c_noalloc(u, P, gout, glse)
+    oo = torch.empty(3, 32, 128, dtype=torch.bfloat16, device=u.q.device)
+    ol = torch.empty(3, 32, dtype=torch.float32, device=u.q.device)
+    for r in range(3):
+        gout.fill_(float("nan"))
+        glse.fill_(float("nan"))
+        c_noalloc(uo, 64 - 16 * r, oo, ol)       # eager, another size: overwrites the workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"replay {r}")
+        assert torch.equal(gout, ref_out) and torch.equal(glse, ref_lse), f"replay {r} differs from the eager call"
