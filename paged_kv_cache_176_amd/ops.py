@@ -125,9 +125,11 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, device) -> ctypes.c_void_p:
+    """The given stream, or the current stream of the tensors' GPU (not of the current device,
+    which may be another GPU)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -276,7 +278,7 @@ def cache_write(key: torch.Tensor, value: Optional[torch.Tensor], slot_mapping: 
     _check(_lib.attn_cache_write(
         _ptr(key), key.stride(0), key.stride(1),
         _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
-        _ptr(slot_mapping), key.shape[0], ctypes.byref(d), _stream(stream)))
+        _ptr(slot_mapping), key.shape[0], ctypes.byref(d), _stream(stream, key.device)))
 
 
 def splitkv_workspace_bytes(rows: int, num_q_heads: int, head_dim_v: int, num_partitions: int) -> int:
@@ -375,7 +377,7 @@ def decode_splitkv(q: torch.Tensor, cache: CacheDesc, block_tables: torch.Tensor
         _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy), _ptr(ws),
         ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
-        _stream(stream)))
+        _stream(stream, q.device)))
     return out, out_lse, ws
 
 
@@ -401,7 +403,7 @@ def decode_splitkv_noalloc(q: torch.Tensor, cache: CacheDesc, block_tables: torc
     _check(_lib.attn_decode_splitkv_noalloc(
         _ptr(q), q.stride(0), q.stride(1), B, Hq, ctypes.byref(d), _ptr(block_tables), block_tables.stride(0),
         _ptr(seq_lens), float(softmax_scale), num_partitions, _policy(split_policy), _ptr(out), _ptr(out_lse),
-        _sinks(sinks, Hq), _stream(stream)))
+        _sinks(sinks, Hq), _stream(stream, q.device)))
     return out, out_lse
 
 
@@ -437,7 +439,7 @@ def decode_splitkv_append(q: torch.Tensor, key: torch.Tensor, value: Optional[to
         _ptr(value), value.stride(0) if value is not None else 0, value.stride(1) if value is not None else 0,
         _ptr(slot_mapping), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
-        _stream(stream))
+        _stream(stream, q.device))
     if prepare:
         return PreparedCall(_lib.attn_decode_splitkv_append, args,
                             (q, key, value, slot_mapping, block_tables, seq_lens, sinks, d), out, out_lse, ws)
@@ -463,7 +465,7 @@ def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torc
     if with_lse and out_lse is None:
         out_lse = torch.empty(rows, Hq, dtype=torch.float32, device=part_out.device)
     _check(_lib.attn_merge_lse(_ptr(part_out), _ptr(part_lse), rows, Hq, Dv, P, _ptr(out), _ptr(out_lse),
-                               _sinks(sinks, Hq), _stream(stream)))
+                               _sinks(sinks, Hq), _stream(stream, part_out.device)))
     return out, out_lse
 
 
@@ -485,7 +487,7 @@ def prefill_causal(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: tor
     _check(_lib.attn_prefill_causal(
         _ptr(q), q.stride(0), q.stride(1), _ptr(query_start_loc), seq_lens.numel(), T, max_query_len, Hq,
         ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), float(softmax_scale),
-        _ptr(out), _ptr(out_lse), _sinks(sinks, Hq), _stream(stream)))
+        _ptr(out), _ptr(out_lse), _sinks(sinks, Hq), _stream(stream, q.device)))
     return out, out_lse
 
 
@@ -513,7 +515,7 @@ def verify(q: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tenso
         ctypes.byref(d), _ptr(block_tables), block_tables.stride(0), _ptr(seq_lens), ctypes.c_float(softmax_scale),
         num_partitions, _policy(split_policy), _ptr(ws), ws.numel() * ws.element_size(),
         None if partials_only else _ptr(out), None if partials_only else _ptr(out_lse), _sinks(sinks, Hq),
-        _stream(stream))
+        _stream(stream, q.device))
     if prepare:
         return PreparedCall(_lib.attn_verify, args, (q, query_start_loc, seq_lens, block_tables, sinks, d), out,
                             out_lse, ws)
